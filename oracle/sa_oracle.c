@@ -1,0 +1,203 @@
+/*
+ * Oracle for masked sparse attention (forward).  TEST INFRASTRUCTURE ONLY.
+ *
+ * This file is the plain, slow, obviously correct CPU definition that the
+ * GPU library is checked against.  Only the test suite, the smoke check and
+ * the bench's CPU-baseline leg may load it.  It shares no code, header or
+ * constant with the product library; the two are compiled separately and
+ * neither includes or links the other.
+ *
+ * Arithmetic is fp64 throughout.  Inputs arrive as fp32 arrays (bf16 inputs
+ * are widened to fp32 exactly before they get here) and are widened to fp64
+ * exactly.  The result is never rounded.
+ *
+ * Sources (cited by page title and section):
+ *   - "Sparse attention" (glossary.selfmadequant.com), section "Choose the
+ *     available reads": y_i = sum_{j in S_i} a_ij v_j with a_ij the softmax of
+ *     q_i.k_j / sqrt(d_k) renormalised over S_i only.
+ *   - "Attention variants" (sreshtalluri.github.io), section 1 "Intuition" and
+ *     section 4 "Build it from scratch": causal rule j <= i, window i-j < w
+ *     counting the query, strided columns, global rows and columns, and the
+ *     union-of-rules composition.
+ *   - "Sparse attention" (octlm.ramaa.tech lab note), section "One mask
+ *     function for every pattern": window 0 means the full causal triangle;
+ *     strided columns at multiples of s (phase 0).
+ *   - "Sparse Attention" (ai360xpert.com), "How It Actually Works": a
+ *     non-causal local neighbourhood on either side, read as a radius r.
+ *
+ * Mask rule used here (the plainest reading that covers every page):
+ *   allowed(i,j) = C(i,j) and ( L(i,j) or St(j) or Gl(i,j) )
+ *   C  : causal -> j <= i ; bidirectional -> always
+ *   L  : causal -> window == 0 or i - j < window
+ *        bidirectional -> no radius given or |i - j| <= radius
+ *   St : stride > 0 and j mod stride == phase
+ *   Gl : i in G or j in G     (G = union of half-open index ranges)
+ * In causal mode C is applied to the global term too, so a global token
+ * never reads or is read from the future ("Attention variants", section 4:
+ * global tokens in a decoder must stay causal).
+ *
+ * Parity pins: see the module docstring of oracle/__init__.py.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    int32_t causal;      /* 1: causal, 0: bidirectional */
+    int32_t has_radius;  /* bidirectional only: 1 if a radius was given */
+    int64_t window;      /* causal only: 0 means unlimited */
+    int64_t radius;      /* bidirectional only */
+    int64_t stride;      /* 0 means no strided columns */
+    int64_t phase;       /* 0 <= phase < stride */
+    int32_t n_global;    /* number of half-open ranges in lo/hi */
+    int32_t pad_;
+    const int64_t* global_lo;
+    const int64_t* global_hi;
+} oracle_mask;
+
+static int in_global(const oracle_mask* m, int64_t x) {
+    for (int32_t r = 0; r < m->n_global; ++r)
+        if (x >= m->global_lo[r] && x < m->global_hi[r]) return 1;
+    return 0;
+}
+
+/* The rule of "allowed", one (query, key) pair at a time. */
+int oracle_allowed(const oracle_mask* m, int64_t i, int64_t j) {
+    int causal_ok = m->causal ? (j <= i) : 1;
+    if (!causal_ok) return 0;
+    int local;
+    if (m->causal) {
+        local = (m->window == 0) ? 1 : (i - j < m->window);
+    } else {
+        int64_t dist = i > j ? i - j : j - i;
+        local = m->has_radius ? (dist <= m->radius) : 1;
+    }
+    int strided = (m->stride > 0) && (j % m->stride == m->phase);
+    int global = in_global(m, i) || in_global(m, j);
+    return local || strided || global;
+}
+
+/* S_i written out as a sorted list by scanning every key; returns |S_i|. */
+int64_t oracle_row_set(const oracle_mask* m, int64_t T, int64_t i, int64_t* out) {
+    int64_t n = 0;
+    for (int64_t j = 0; j < T; ++j)
+        if (oracle_allowed(m, i, j)) {
+            if (out) out[n] = j;
+            ++n;
+        }
+    return n;
+}
+
+/* E = sum_i |S_i| by scanning all T*T pairs; optional per-row counts. */
+int64_t oracle_count(const oracle_mask* m, int64_t T, int64_t* row_counts) {
+    int64_t total = 0;
+#pragma omp parallel for schedule(dynamic, 64) reduction(+ : total)
+    for (int64_t i = 0; i < T; ++i) {
+        int64_t c = oracle_row_set(m, T, i, NULL);
+        if (row_counts) row_counts[i] = c;
+        total += c;
+    }
+    return total;
+}
+
+/* Tile classes, decided by counting allowed pairs among a tile's in-range
+ * cells (rows i < T and keys j < T): 0 = no allowed pair, 1 = every in-range
+ * pair allowed, 2 = some but not all. */
+void oracle_tile_map(const oracle_mask* m, int64_t T, int64_t bq, int64_t bk,
+                     uint8_t* map) {
+    int64_t nqb = (T + bq - 1) / bq, nkb = (T + bk - 1) / bk;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t qb = 0; qb < nqb; ++qb) {
+        for (int64_t kb = 0; kb < nkb; ++kb) {
+            int64_t cells = 0, allowed = 0;
+            for (int64_t i = qb * bq; i < (qb + 1) * bq && i < T; ++i)
+                for (int64_t j = kb * bk; j < (kb + 1) * bk && j < T; ++j) {
+                    ++cells;
+                    allowed += oracle_allowed(m, i, j);
+                }
+            map[qb * nkb + kb] = allowed == 0 ? 0 : (allowed == cells ? 1 : 2);
+        }
+    }
+}
+
+/*
+ * Forward pass for a list of rows.  Tensors are [BH][T][d] fp32, row-major.
+ * rows[r] = bh * T + i selects query i of head bh.  For each selected row:
+ *   1. S_i by scanning every key,
+ *   2. s_j = (q_i . k_j) / sqrt(d),
+ *   3. mx = max_j s_j,
+ *   4. l = sum_j exp(s_j - mx),
+ *   5. o = (sum_j exp(s_j - mx) v_j) / l,   lse = mx + log(l).
+ * Outputs: O[r][d] and lse[r] in fp64, nset[r] = |S_i| (any may be NULL
+ * except O).  Returns 0, or -1 if a row is out of range or memory runs out.
+ * An empty S_i (not reachable through the mask grammar, whose window or
+ * radius always keeps the query itself) gives o = 0 and lse = -inf.
+ */
+int oracle_forward_rows(const oracle_mask* m, const float* Q, const float* K,
+                        const float* V, int64_t BH, int64_t T, int64_t d,
+                        const int64_t* rows, int64_t n_rows, double* O,
+                        double* lse, int64_t* nset) {
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= BH * T) return -1;
+    int failed = 0;
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+#pragma omp parallel reduction(| : failed)
+    {
+        int64_t* set = (int64_t*)malloc(sizeof(int64_t) * (size_t)(T > 0 ? T : 1));
+        double* s = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+        double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+        if (!set || !s || !acc) failed = 1;
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            if (failed) continue;
+            int64_t bh = rows[r] / T, i = rows[r] % T;
+            const float* q = Q + (bh * T + i) * d;
+            int64_t n = oracle_row_set(m, T, i, set);
+            if (nset) nset[r] = n;
+            double* o = O + r * d;
+            if (n == 0) {
+                for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+                if (lse) lse[r] = -INFINITY;
+                continue;
+            }
+            double mx = -INFINITY;
+            for (int64_t t = 0; t < n; ++t) {
+                const float* k = K + (bh * T + set[t]) * d;
+                double dot = 0.0;
+                for (int64_t c = 0; c < d; ++c) dot += (double)q[c] * (double)k[c];
+                s[t] = dot * inv_sqrt_d;
+                if (s[t] > mx) mx = s[t];
+            }
+            double l = 0.0;
+            for (int64_t c = 0; c < d; ++c) acc[c] = 0.0;
+            for (int64_t t = 0; t < n; ++t) {
+                double p = exp(s[t] - mx);
+                l += p;
+                const float* v = V + (bh * T + set[t]) * d;
+                for (int64_t c = 0; c < d; ++c) acc[c] += p * (double)v[c];
+            }
+            for (int64_t c = 0; c < d; ++c) o[c] = acc[c] / l;
+            if (lse) lse[r] = mx + log(l);
+        }
+        free(set);
+        free(s);
+        free(acc);
+    }
+    return failed ? -1 : 0;
+}
+
+int oracle_threads(void) {
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}

@@ -1,0 +1,108 @@
+"""Plants plausible mistakes in a private copy of the oracle's C source (on the
+CPU) and checks that the pins reject every one.  The shipped oracle is never
+modified; each mutant is compiled into a temporary directory.
+"""
+import ctypes
+import json
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from block_sparse_masked_spec_amd import inputs
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "sa_oracle.c")
+FACTS = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")))
+
+# (name, original text, planted text)
+MUTANTS = [
+    ("window_excludes_query", "(i - j < m->window)", "(i - j <= m->window)"),
+    ("window_sign_flipped", "(i - j < m->window)", "(j - i < m->window)"),
+    ("causal_dropped", "int causal_ok = m->causal ? (j <= i) : 1;", "int causal_ok = 1;"),
+    ("causal_strict", "int causal_ok = m->causal ? (j <= i) : 1;",
+     "int causal_ok = m->causal ? (j < i) : 1;"),
+    ("radius_strict", "(dist <= m->radius)", "(dist < m->radius)"),
+    ("stride_phase_ignored", "(j % m->stride == m->phase)", "(j % m->stride == 0)"),
+    ("stride_dropped", "return local || strided || global;", "return local || global;"),
+    ("global_rows_dropped", "int global = in_global(m, i) || in_global(m, j);",
+     "int global = in_global(m, j);"),
+    ("global_cols_dropped", "int global = in_global(m, i) || in_global(m, j);",
+     "int global = in_global(m, i);"),
+    ("scale_by_d", "1.0 / sqrt((double)d)", "1.0 / (double)d"),
+    ("no_scale", "1.0 / sqrt((double)d)", "1.0"),
+    ("k_used_as_v", "const float* v = V + (bh * T + set[t]) * d;",
+     "const float* v = K + (bh * T + set[t]) * d;"),
+    ("v_from_query_row", "const float* v = V + (bh * T + set[t]) * d;",
+     "const float* v = V + (bh * T + i) * d;"),
+    ("no_renormalise", "o[c] = acc[c] / l;", "o[c] = acc[c];"),
+    ("max_not_subtracted_in_lse", "lse[r] = mx + log(l);", "lse[r] = log(l);"),
+    ("k_row_is_query_row", "const float* k = K + (bh * T + set[t]) * d;",
+     "const float* k = K + (bh * T + i) * d;"),
+    ("dot_uses_q_twice", "dot += (double)q[c] * (double)k[c];", "dot += (double)q[c] * (double)q[c];"),
+]
+
+
+def _build_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(old, new))
+    so = tmp_path / f"{name}.so"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", str(path),
+                    "-o", str(so), "-lm"], check=True)
+    return str(so)
+
+
+def _pins_pass() -> bool:
+    """A compact run of the pins (counts, sets, library SDPA, identities)."""
+    try:
+        for f in FACTS["counts"]:
+            if oracle.count(f["spec"], f["T"]) != f["allowed"]:
+                return False
+        for f in FACTS["row_sets"]:
+            if oracle.row_set(f["spec"], f["T"], f["row"]) != f["keys"]:
+                return False
+        q, k, v = inputs.qkv(1, 2, 33, 16, "f32", 1)
+        O, lse, _ = oracle.forward_rows("causal", q, k, v)
+        ref = F.scaled_dot_product_attention(q.double(), k.double(), v.double(), is_causal=True)
+        if not np.allclose(O, ref.numpy(), rtol=1e-10, atol=1e-10):
+            return False
+        s = torch.matmul(q.double(), k.double().transpose(-1, -2)) / math.sqrt(16)
+        s = s.masked_fill(~torch.tril(torch.ones(33, 33, dtype=torch.bool)), float("-inf"))
+        if not np.allclose(lse, torch.logsumexp(s, -1).numpy(), rtol=1e-10, atol=1e-10):
+            return False
+        O1, _, _ = oracle.forward_rows("causal;window=1", q, k, v)
+        if not np.array_equal(O1, v.double().numpy()):
+            return False
+        for f in FACTS["row_sets"]:
+            q0 = torch.zeros(1, 1, f["T"], 8)
+            _, k8, v8 = inputs.qkv(1, 1, f["T"], 8, "f32", 2)
+            Om, _, _ = oracle.forward_rows(f["spec"], q0, k8, v8, rows=[(0, 0, f["row"])])
+            if not np.allclose(Om[0], v8[0, 0, f["keys"]].double().mean(0).numpy(), atol=1e-12):
+                return False
+    except Exception:
+        return False
+    return True
+
+
+def test_unmutated_oracle_passes_compact_pins():
+    assert _pins_pass()
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_every_planted_mistake_is_caught(tmp_path, name, old, new, monkeypatch):
+    so = _build_mutant(tmp_path, name, old, new)
+    saved_lib, saved_path = oracle._lib, oracle._LIB_PATH
+    try:
+        monkeypatch.setattr(oracle, "_LIB_PATH", so)
+        oracle._lib = None
+        assert not _pins_pass(), f"pins did not catch mutant {name}"
+    finally:
+        oracle._lib = saved_lib
+        monkeypatch.setattr(oracle, "_LIB_PATH", saved_path)
+        oracle._lib = None

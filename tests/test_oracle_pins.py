@@ -1,0 +1,356 @@
+"""Pins for the oracle: facts fixed by the pages and by mathematics, never by
+the oracle itself.  CPU only.
+
+Each test names what it pins and which plausible mistake would fail it.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from block_sparse_masked_spec_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")
+FACTS = json.load(open(GOLDEN))
+
+
+# ---------------------------------------------------------------- mask counts
+@pytest.mark.parametrize("fact", FACTS["counts"], ids=lambda f: f"{f['spec']}@T{f['T']}")
+def test_page_printed_counts(fact):
+    """Printed allowed-cell counts (11, 21, 136, 58, 52, 100, 256).  Fails on a
+    window that does not count the query, a wrong stride phase, a global rule
+    that misses rows or columns, or a dropped causal term."""
+    assert oracle.count(fact["spec"], fact["T"]) == fact["allowed"], fact["cite"]
+
+
+@pytest.mark.parametrize("fact", FACTS["row_sets"], ids=lambda f: f"{f['spec']}@{f['row']}")
+def test_page_printed_row_sets(fact):
+    assert oracle.row_set(fact["spec"], fact["T"], fact["row"]) == fact["keys"], fact["cite"]
+
+
+@pytest.mark.parametrize("fact", FACTS["row_sizes"], ids=lambda f: f["spec"])
+def test_page_printed_row_sizes(fact):
+    total, rows = oracle.count(fact["spec"], fact["T"], per_row=True)
+    assert rows.tolist() == fact["sizes"], fact["cite"]
+    assert total == sum(fact["sizes"])
+
+
+@pytest.mark.parametrize("fact", FACTS["strided_columns"], ids=lambda f: f["spec"])
+def test_page_printed_strided_columns(fact):
+    """With the window 2, the keys a late query reads beyond its window are
+    exactly the printed long-range columns."""
+    T = fact["T"]
+    last = T - 1
+    far = [j for j in oracle.row_set(fact["spec"], T, last) if last - j >= 2]
+    assert far == [c for c in fact["columns"] if last - c >= 2], fact["cite"]
+    # every printed column is visible to every query at or after it
+    for c in fact["columns"]:
+        for i in range(c, T):
+            assert oracle.allowed(fact["spec"], i, c)
+
+
+@pytest.mark.parametrize("n,w", [(6, 2), (16, 4), (32, 8), (100, 1), (100, 7), (257, 64),
+                                 (1000, 128), (512, 512), (4096, 4096)])
+def test_closed_form_window_count(n, w):
+    """E = n*w - w*(w-1)/2 for n >= w ("Sparse attention",
+    glossary.selfmadequant.com, section 'When the cost is linear').  The
+    n=32, w=8 case is the practice exercise of "Attention variants", section 6
+    (answer 228 from the closed form; the page prints none)."""
+    e = n * w - w * (w - 1) // 2
+    assert oracle.count(f"causal;window={w}", n) == e
+    if (n, w) == (32, 8):
+        assert e == 228
+
+
+@pytest.mark.parametrize("n", [1, 2, 6, 16, 33, 300])
+def test_full_causal_and_window_at_least_T(n):
+    """Window 0 is the full causal triangle ("Sparse attention", octlm lab
+    note, 'What happened?'); a window of n equals causal ("Attention
+    variants", section 4, the script's assertion); bidir with no radius is
+    every pair."""
+    tri = n * (n + 1) // 2
+    assert oracle.count("causal", n) == tri
+    assert oracle.count("causal;window=0", n) == tri
+    assert oracle.count(f"causal;window={n}", n) == tri
+    assert oracle.count(f"causal;window={n + 5}", n) == tri
+    assert oracle.count("bidir", n) == n * n
+
+
+def test_window_last_row_reads_w_keys():
+    """"A window of 4 turns it into a band. The last row reads only 4 keys"
+    (restated from "Sparse attention", octlm lab note, 'What happened?')."""
+    for T in (5, 16, 100):
+        assert len(oracle.row_set("causal;window=4", T, T - 1)) == 4
+
+
+def test_phase_zero_matches_lab_note_mask_function():
+    """The lab note's mask function ("Sparse attention", octlm, section 'One
+    mask function for every pattern'): distance >= 0 and (distance < window or
+    column % stride == 0), restated with torch ops."""
+    for T, w, s in [(64, 8, 16), (100, 5, 7), (33, 1, 4)]:
+        rows = torch.arange(T).unsqueeze(1)
+        cols = torch.arange(T).unsqueeze(0)
+        dist = rows - cols
+        ref = (dist >= 0) & ((dist < w) | (cols % s == 0))
+        got = oracle.dense_mask(f"causal;window={w};stride={s}", T)
+        assert np.array_equal(got, ref.numpy())
+        assert oracle.count(f"causal;window={w};stride={s}", T) == int(ref.sum())
+
+
+def test_radius_global_p5_counts():
+    """Non-causal radius + first-g globals, restating the local+global toy of
+    "Sparse Attention" (ai360xpert.com), 'Show Me the Code' (lo = i - W//2,
+    hi = i + W//2 + 1, first g rows and columns set).  Its printed 743 does not
+    follow from its own code (the code gives 1016); the code is the pin."""
+    n, W, g = 64, 8, 4
+    m = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        lo, hi = max(0, i - W // 2), min(n, i + W // 2 + 1)
+        m[i, lo:hi] = True
+    m[:g, :] = True
+    m[:, :g] = True
+    assert int(m.sum()) == 1016
+    assert oracle.count(f"bidir;radius={W // 2};global=0:{g}", n) == 1016
+
+
+def test_global_tokens_stay_causal_in_decoder():
+    """In causal mode a global token neither reads the future nor is read by
+    earlier queries ("Attention variants", section 4: global tokens must stay
+    causal in a decoder)."""
+    T = 16
+    spec = "causal;window=2;global=5"
+    for i in range(T):
+        for j in range(T):
+            if j > i:
+                assert not oracle.allowed(spec, i, j)
+    assert oracle.row_set(spec, T, 5) == [0, 1, 2, 3, 4, 5]
+    assert 5 in oracle.row_set(spec, T, 15)
+
+
+@pytest.mark.parametrize("spec", [
+    "causal;window=3;stride=5;phase=2",
+    "bidir;radius=1;stride=4;global=0,7:9",
+    "causal;global=2:4",
+    "bidir;radius=0;global=10",
+    "causal;window=1;stride=3",
+])
+def test_dense_mask_agrees_with_pairwise_rule(spec):
+    """The array formulation and the pair-by-pair rule are two codings of the
+    same definition; they must agree cell by cell on tiny T (brute force)."""
+    T = 23
+    dense = oracle.dense_mask(spec, T)
+    for i in range(T):
+        assert [j for j in range(T) if dense[i, j]] == oracle.row_set(spec, T, i)
+
+
+@pytest.mark.parametrize("T,bq,bk", [(16, 4, 4), (23, 8, 5), (40, 16, 16), (7, 16, 16)])
+def test_tile_map_from_dense_mask(T, bq, bk):
+    """Tile classes from counting allowed cells of the dense mask per tile."""
+    spec = "causal;window=3;stride=5;phase=1;global=9"
+    dense = oracle.dense_mask(spec, T)
+    tm = oracle.tile_map(spec, T, bq, bk)
+    for qb in range(tm.shape[0]):
+        for kb in range(tm.shape[1]):
+            blk = dense[qb * bq:(qb + 1) * bq, kb * bk:(kb + 1) * bk]
+            want = 0 if not blk.any() else (1 if blk.all() else 2)
+            assert tm[qb, kb] == want
+
+
+# ------------------------------------------------------------------- outputs
+def _rand(B, H, T, d, seed, dtype="f32"):
+    return inputs.qkv(B, H, T, d, dtype, seed)
+
+
+def test_window_one_is_identity():
+    """w = 1: S_i = {i}, the weight is exactly 1, so o_i = v_i exactly.  Fails
+    on a transposed K/V, a wrong value index, or a bad normalisation."""
+    q, k, v = _rand(2, 3, 37, 16, 1)
+    O, lse, n = oracle.forward_rows("causal;window=1", q, k, v)
+    assert np.array_equal(O, v.double().numpy())
+    assert (n == 1).all()
+    s = (q.double() * k.double()).sum(-1) / math.sqrt(16)
+    assert np.allclose(lse, s.numpy(), rtol=0, atol=1e-12)
+
+
+def _mean_of(v, keys):
+    return v[..., keys, :].double().mean(dim=-2).numpy()
+
+
+def test_zero_query_gives_mean_over_printed_sets():
+    """q = 0 makes every allowed score 0, so o_i is the plain mean of v over
+    S_i: this pins membership and renormalisation together, against the
+    pages' printed sets."""
+    for fact in FACTS["row_sets"]:
+        T = fact["T"]
+        q, k, v = _rand(1, 2, T, 8, 2)
+        q = torch.zeros_like(q)
+        O, _, _ = oracle.forward_rows(fact["spec"], q, k, v, rows=[(0, 1, fact["row"])])
+        assert np.allclose(O[0], _mean_of(v[0, 1], fact["keys"]), rtol=0, atol=1e-12)
+
+
+def test_zero_query_window_interval():
+    """For a causal window the set is the interval [max(0, t-W+1), t]
+    ("Sparse and sliding-window attention", getnybble.com, section 'Sliding
+    window attention')."""
+    T, W = 50, 7
+    q, k, v = _rand(1, 1, T, 8, 3)
+    q = torch.zeros_like(q)
+    O, _, _ = oracle.forward_rows(f"causal;window={W}", q, k, v)
+    for t in range(T):
+        keys = list(range(max(0, t - W + 1), t + 1))
+        assert np.allclose(O[0, 0, t], _mean_of(v[0, 0], keys), rtol=0, atol=1e-12)
+
+
+def _sdpa64(q, k, v, mask=None, is_causal=False):
+    return F.scaled_dot_product_attention(
+        q.double(), k.double(), v.double(), attn_mask=mask, is_causal=is_causal).numpy()
+
+
+@pytest.mark.parametrize("T,d", [(1, 16), (17, 16), (64, 32), (130, 64)])
+def test_full_causal_matches_library_sdpa(T, d):
+    """Window 0 reduces to textbook causal attention: torch's CPU SDPA in fp64
+    with is_causal.  Fails on a wrong scale (1/d vs 1/sqrt(d)), a transposed
+    operand or a missing renormalisation."""
+    q, k, v = _rand(2, 2, T, d, 4)
+    O, _, _ = oracle.forward_rows("causal", q, k, v)
+    assert np.allclose(O, _sdpa64(q, k, v, is_causal=True), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("T,d", [(1, 16), (40, 64), (97, 128)])
+def test_bidir_unlimited_matches_library_sdpa(T, d):
+    q, k, v = _rand(1, 3, T, d, 5)
+    O, _, _ = oracle.forward_rows("bidir", q, k, v)
+    assert np.allclose(O, _sdpa64(q, k, v), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("T,w", [(33, 1), (64, 5), (100, 16), (77, 80)])
+def test_window_matches_library_band(T, w):
+    """A causal window as a band built by torch's tril/triu (a library routine,
+    not this oracle's rule), fed to CPU SDPA in fp64; also lse against
+    torch.logsumexp over the same band."""
+    q, k, v = _rand(1, 2, T, 32, 6)
+    ones = torch.ones(T, T, dtype=torch.bool)
+    band = torch.tril(ones) & torch.triu(ones, diagonal=-(w - 1))
+    O, lse, n = oracle.forward_rows(f"causal;window={w}", q, k, v)
+    assert np.allclose(O, _sdpa64(q, k, v, mask=band), rtol=1e-12, atol=1e-12)
+    s = torch.matmul(q.double(), k.double().transpose(-1, -2)) / math.sqrt(32)
+    s = s.masked_fill(~band, float("-inf"))
+    assert np.allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=1e-12, atol=1e-12)
+    assert np.array_equal(n[0, 0], band.sum(-1).numpy())
+
+
+@pytest.mark.parametrize("T,r", [(40, 0), (64, 3), (50, 60)])
+def test_radius_matches_library_band(T, r):
+    q, k, v = _rand(1, 1, T, 16, 7)
+    ones = torch.ones(T, T, dtype=torch.bool)
+    band = torch.tril(ones, diagonal=r) & torch.triu(ones, diagonal=-r)
+    O, _, _ = oracle.forward_rows(f"bidir;radius={r}", q, k, v)
+    assert np.allclose(O, _sdpa64(q, k, v, mask=band), rtol=1e-12, atol=1e-12)
+
+
+SPECS_MIXED = [
+    "causal;window=2;stride=4;phase=3",
+    "causal;window=5;stride=8",
+    "bidir;radius=3;stride=6;phase=1;global=0:3,20",
+    "causal;window=4;global=7,30:32",
+    "bidir;radius=2;global=0",
+]
+
+
+@pytest.mark.parametrize("spec", SPECS_MIXED)
+def test_loops_match_dense_formulation(spec):
+    """The per-row loops against the dense materialise-mask-softmax recipe."""
+    q, k, v = _rand(2, 2, 41, 16, 8)
+    O, _, _ = oracle.forward_rows(spec, q, k, v)
+    assert np.allclose(O, oracle.dense_forward(spec, q, k, v), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("spec", SPECS_MIXED)
+def test_mixed_masks_match_library_sdpa_with_page_rule_mask(spec):
+    """Strided and global patterns: torch SDPA (fp64) with a boolean mask
+    built by the pages' composition rules ("True means may attend",
+    "Attention variants", section 4 'Use the library')."""
+    T = 41
+    q, k, v = _rand(1, 2, T, 16, 9)
+    mask = torch.from_numpy(oracle.dense_mask(spec, T))
+    O, _, _ = oracle.forward_rows(spec, q, k, v)
+    assert np.allclose(O, _sdpa64(q, k, v, mask=mask), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("spec", SPECS_MIXED + ["causal", "bidir"])
+def test_key_shift_invariance(spec):
+    """Adding one vector u to every key shifts each row's logits by a constant,
+    which the renormalised softmax removes."""
+    q, k, v = _rand(1, 2, 29, 16, 10)
+    u = torch.randn(16, generator=torch.Generator().manual_seed(11))
+    O1, _, _ = oracle.forward_rows(spec, q, k, v)
+    O2, _, _ = oracle.forward_rows(spec, q, (k.double() + u.double()).float(), v)
+    # k + u is rounded to fp32, so compare loosely
+    assert np.allclose(O1, O2, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("spec", SPECS_MIXED)
+def test_value_affine_invariance(spec):
+    """Weights sum to 1 over S_i ("Choose the available reads"), so
+    V -> a V + b gives O -> a O + b."""
+    q, k, v = _rand(1, 1, 29, 16, 12)
+    b = np.linspace(-1.0, 1.0, 16)
+    O1, _, _ = oracle.forward_rows(spec, q, k, v)
+    O2, _, _ = oracle.forward_rows(spec, q, k, (2.0 * v.double() + torch.from_numpy(b)).float())
+    assert np.allclose(O2, 2.0 * O1 + b, rtol=1e-6, atol=1e-6)
+
+
+def test_deleting_weights_without_renormalising_differs():
+    """Negative pin: a full softmax with the excluded weights zeroed afterwards
+    is a different operation ("Choose the available reads")."""
+    spec = "causal;window=3"
+    T, d = 20, 16
+    q, k, v = _rand(1, 1, T, d, 13)
+    O, _, _ = oracle.forward_rows(spec, q, k, v)
+    s = torch.matmul(q.double(), k.double().transpose(-1, -2)) / math.sqrt(d)
+    causal = torch.tril(torch.ones(T, T, dtype=torch.bool))
+    w = torch.softmax(s.masked_fill(~causal, float("-inf")), dim=-1)
+    w = w * torch.from_numpy(oracle.dense_mask(spec, T))
+    wrong = torch.matmul(w, v.double()).numpy()
+    assert np.abs(wrong[0, 0, 3:] - O[0, 0, 3:]).max() > 1e-3
+
+
+def test_bf16_inputs_are_consumed_exactly():
+    """bf16 inputs widen exactly: the oracle on bf16 tensors equals the oracle
+    on the same values stored as fp32."""
+    q, k, v = inputs.qkv(1, 2, 40, 32, "bf16", 14)
+    O1, _, _ = oracle.forward_rows("causal;window=9", q, k, v)
+    O2, _, _ = oracle.forward_rows("causal;window=9", q.float(), k.float(), v.float())
+    assert np.array_equal(O1, O2)
+
+
+def test_selected_rows_equal_full_run():
+    spec = "bidir;radius=3;stride=6;phase=1;global=0:3,20"
+    q, k, v = _rand(2, 3, 31, 16, 15)
+    full, lse_full, _ = oracle.forward_rows(spec, q, k, v)
+    rows = [(0, 0, 0), (1, 2, 30), (0, 1, 20), (1, 0, 7)]
+    O, lse, _ = oracle.forward_rows(spec, q, k, v, rows=rows)
+    for r, (b, h, i) in enumerate(rows):
+        assert np.array_equal(O[r], full[b, h, i])
+        assert lse[r] == lse_full[b, h, i]
+
+
+# ------------------------------------------------------------------ the spec
+@pytest.mark.parametrize("bad", [
+    "", "sparse", "causal;radius=3", "bidir;window=3", "causal;window=3;window=4",
+    "causal;phase=1", "causal;stride=4;phase=4", "causal;window=-1", "causal;foo=1",
+    "bidir;global=5:5", "bidir;global=a", "causal;window", "causal;stride=4;phase=x",
+])
+def test_oracle_parser_rejects(bad):
+    with pytest.raises(oracle.OracleSpecError):
+        oracle.parse_spec(bad)
+
+
+def test_oracle_parser_accepts_whitespace_and_ranges():
+    m = oracle.parse_spec(" bidir ; radius = 2 ; global = 0 , 5:8 ")
+    assert not m.causal and m.radius == 2 and m.globals_ == [(0, 1), (5, 8)]
