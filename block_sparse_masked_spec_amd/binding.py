@@ -1,0 +1,198 @@
+"""ctypes binding of libsparse_attn.so (see include/sparse_attn.h).
+
+Argument marshalling only: every step of the computation runs in the
+library.  Functions keep the C names.  Tensor arguments may be torch
+tensors (their ``data_ptr()`` is passed) or raw integer device addresses.
+A non-OK status raises ``SparseAttnError`` carrying the status code.
+
+The library is loaded after ``torch`` so that it binds to the HIP runtime
+torch already loaded (same SONAME), sharing devices and streams with it.
+If the library is missing this module raises on first use -- there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads torch's HIP runtime first)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
+
+SA_OK = 0
+SA_ERR_SPEC = -1
+SA_ERR_RANGE = -2
+SA_ERR_SHAPE = -3
+SA_ERR_UNSUPPORTED = -4
+SA_ERR_NULL = -5
+SA_ERR_ALIAS = -6
+SA_ERR_HIP = -7
+SA_ERR_ALIGN = -8
+SA_ERR_NOMEM = -9
+
+SA_TILE_EMPTY, SA_TILE_FULL, SA_TILE_PARTIAL = 0, 1, 2
+SA_DTYPE_BF16, SA_DTYPE_F32 = 0, 1
+SA_MAX_GLOBAL_RANGES = 64
+
+EXPORTED = [
+    "sparse_attn_fwd", "sparse_attn_fwd_f32", "sparse_attn_parse", "sparse_attn_count",
+    "sparse_attn_tile_map", "sparse_attn_tile_shape", "sparse_attn_plan_info",
+    "sparse_attn_strerror", "sparse_attn_release_cache",
+]
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+class sa_mask(ctypes.Structure):
+    _fields_ = [
+        ("causal", ctypes.c_int32), ("has_radius", ctypes.c_int32),
+        ("window", ctypes.c_int64), ("radius", ctypes.c_int64),
+        ("stride", ctypes.c_int64), ("phase", ctypes.c_int64),
+        ("n_global", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("global_lo", ctypes.c_int64 * SA_MAX_GLOBAL_RANGES),
+        ("global_hi", ctypes.c_int64 * SA_MAX_GLOBAL_RANGES),
+    ]
+
+
+class sa_plan_info(ctypes.Structure):
+    _fields_ = [
+        ("bq", ctypes.c_int32), ("bk", ctypes.c_int32),
+        ("n_qb", ctypes.c_int32), ("n_kb", ctypes.c_int32),
+        ("inplace_tiles", ctypes.c_int64), ("masked_tiles", ctypes.c_int64),
+        ("gathered_tiles", ctypes.c_int64), ("gathered_keys", ctypes.c_int64),
+        ("executed_cells", ctypes.c_int64), ("allowed_cells", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def load():
+    """Load (once) and return the library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FileNotFoundError(
+            f"{LIB_PATH} is missing: build it with `python -m block_sparse_masked_spec_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, cs = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_char_p
+    fwd_args = [vp, vp, vp, vp, i32, i32, i32, i32, cs, vp]
+    lib.sparse_attn_fwd.argtypes = fwd_args
+    lib.sparse_attn_fwd.restype = i32
+    lib.sparse_attn_fwd_f32.argtypes = fwd_args
+    lib.sparse_attn_fwd_f32.restype = i32
+    lib.sparse_attn_parse.argtypes = [cs, ctypes.POINTER(sa_mask)]
+    lib.sparse_attn_parse.restype = i32
+    lib.sparse_attn_count.argtypes = [cs, i32, ctypes.POINTER(i64), vp]
+    lib.sparse_attn_count.restype = i32
+    lib.sparse_attn_tile_map.argtypes = [cs, i32, i32, i32, vp]
+    lib.sparse_attn_tile_map.restype = i32
+    lib.sparse_attn_tile_shape.argtypes = [i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.sparse_attn_tile_shape.restype = i32
+    lib.sparse_attn_plan_info.argtypes = [cs, i32, i32, i32, ctypes.POINTER(sa_plan_info)]
+    lib.sparse_attn_plan_info.restype = i32
+    lib.sparse_attn_strerror.argtypes = [i32]
+    lib.sparse_attn_strerror.restype = cs
+    lib.sparse_attn_release_cache.argtypes = []
+    lib.sparse_attn_release_cache.restype = None
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load().sparse_attn_strerror(int(status)).decode()
+
+
+def _check(status: int, where: str) -> int:
+    if status != SA_OK:
+        raise SparseAttnError(status, where)
+    return status
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream_handle(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _spec(s) -> bytes:
+    return s.encode() if isinstance(s, str) else s
+
+
+def sparse_attn_fwd(Q, K, V, O, B, H, T, d, mask_spec, stream=None):
+    """bf16 forward; stream defaults to torch's current stream."""
+    return _check(load().sparse_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), B, H, T, d,
+                                         _spec(mask_spec), _stream_handle(stream)),
+                  "sparse_attn_fwd")
+
+
+def sparse_attn_fwd_f32(Q, K, V, O, B, H, T, d, mask_spec, stream=None):
+    """fp32 forward; stream defaults to torch's current stream."""
+    return _check(load().sparse_attn_fwd_f32(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), B, H, T, d,
+                                             _spec(mask_spec), _stream_handle(stream)),
+                  "sparse_attn_fwd_f32")
+
+
+def sparse_attn_parse(mask_spec) -> sa_mask:
+    m = sa_mask()
+    _check(load().sparse_attn_parse(_spec(mask_spec), ctypes.byref(m)), "sparse_attn_parse")
+    return m
+
+
+def sparse_attn_count(mask_spec, T, row_counts=False):
+    """Returns E, or (E, int32 numpy row counts) when row_counts is True."""
+    import numpy as np
+    total = ctypes.c_int64(0)
+    rows = np.zeros(max(T, 1), dtype=np.int32) if row_counts else None
+    _check(load().sparse_attn_count(_spec(mask_spec), T, ctypes.byref(total),
+                                    rows.ctypes.data if row_counts else None),
+           "sparse_attn_count")
+    return (total.value, rows[:T]) if row_counts else total.value
+
+
+def sparse_attn_tile_map(mask_spec, T, bq, bk):
+    """Returns a uint8 numpy array [ceil(T/bq), ceil(T/bk)] of SA_TILE_*."""
+    import numpy as np
+    nqb, nkb = -(-T // bq) if bq > 0 else 0, -(-T // bk) if bk > 0 else 0
+    out = np.zeros(max(nqb * nkb, 1), dtype=np.uint8)
+    _check(load().sparse_attn_tile_map(_spec(mask_spec), T, bq, bk, out.ctypes.data),
+           "sparse_attn_tile_map")
+    return out[:nqb * nkb].reshape(nqb, nkb)
+
+
+def sparse_attn_tile_shape(d, dtype=SA_DTYPE_BF16):
+    bq, bk = ctypes.c_int(0), ctypes.c_int(0)
+    _check(load().sparse_attn_tile_shape(d, dtype, ctypes.byref(bq), ctypes.byref(bk)),
+           "sparse_attn_tile_shape")
+    return bq.value, bk.value
+
+
+def sparse_attn_plan_info(mask_spec, T, d, dtype=SA_DTYPE_BF16) -> dict:
+    info = sa_plan_info()
+    _check(load().sparse_attn_plan_info(_spec(mask_spec), T, d, dtype, ctypes.byref(info)),
+           "sparse_attn_plan_info")
+    return {name: getattr(info, name) for name, _ in sa_plan_info._fields_}
+
+
+def sparse_attn_strerror(status):
+    return strerror(status)
+
+
+def sparse_attn_release_cache():
+    load().sparse_attn_release_cache()

@@ -1,0 +1,161 @@
+// Host planner: allowed-pair counts, exact tile classes and the execution
+// plan of the fused kernel.
+//
+// Tile skipping follows "Sparse and sliding-window attention" (getnybble.com,
+// section "Implementation": skip tiles outside the band) and "Attention
+// variants" (sreshtalluri.github.io, section 4 "Use the library": skip fully
+// masked blocks).  Strided and global columns would make every key tile
+// non-empty, so the plan runs them apart: for each query block, the key
+// tiles that meet the band (or every tile, if the block holds a global row)
+// run in place, and the strided/global keys outside those tiles are
+// gathered into dense tiles of their own.
+#include <algorithm>
+#include <numeric>
+
+#include "internal.hpp"
+
+namespace sa {
+
+MaskRule::MaskRule(const sa_mask& m, int64_t T) : m_(m), T_(T), colpre_(T + 1, 0), rowpre_(T + 1, 0) {
+    std::vector<uint8_t> glob(T, 0);
+    for (int k = 0; k < m.n_global; ++k)
+        for (int64_t x = m.global_lo[k]; x < m.global_hi[k] && x < T; ++x) glob[x] = 1;
+    for (int64_t j = 0; j < T; ++j) {
+        bool strided = m.stride > 0 && (j % m.stride) == m.phase;
+        colpre_[j + 1] = colpre_[j] + ((strided || glob[j]) ? 1 : 0);
+        rowpre_[j + 1] = rowpre_[j] + (glob[j] ? 1 : 0);
+    }
+}
+
+int64_t MaskRule::band_lo(int64_t i) const {
+    if (m_.causal) return m_.window == 0 ? 0 : std::max<int64_t>(0, i - m_.window + 1);
+    return m_.has_radius ? std::max<int64_t>(0, i - m_.radius) : 0;
+}
+
+int64_t MaskRule::band_hi(int64_t i) const {
+    if (m_.causal) return i;
+    return m_.has_radius ? std::min<int64_t>(T_ - 1, i + m_.radius) : T_ - 1;
+}
+
+int32_t MaskRule::band_back() const {
+    if (m_.causal) return m_.window == 0 ? INT32_MAX : static_cast<int32_t>(m_.window - 1);
+    return m_.has_radius ? static_cast<int32_t>(m_.radius) : INT32_MAX;
+}
+
+int32_t MaskRule::band_fwd() const {
+    if (m_.causal) return 0;
+    return m_.has_radius ? static_cast<int32_t>(m_.radius) : INT32_MAX;
+}
+
+int64_t MaskRule::allowed_in(int64_t i, int64_t a, int64_t b) const {
+    a = std::max<int64_t>(a, 0);
+    b = std::min<int64_t>(b, key_limit(i) + 1);  // causal cut
+    if (a >= b) return 0;
+    if (row_global(i)) return b - a;
+    int64_t lo = std::max(a, band_lo(i)), hi = std::min(b, band_hi(i) + 1);
+    if (lo >= hi) return col_keys_in(a, b);
+    return (hi - lo) + col_keys_in(a, b) - col_keys_in(lo, hi);
+}
+
+int MaskRule::classify(int64_t q0, int64_t q1, int64_t k0, int64_t k1) const {
+    q1 = std::min(q1, T_);
+    k1 = std::min(k1, T_);
+    if (q0 >= q1 || k0 >= k1) return SA_TILE_EMPTY;
+    if (rows_global_in(q0, q1) == 0) {
+        // Band ends are monotone in i: the first row has the lowest upper
+        // end, the last row the highest lower end.
+        if (k0 >= band_lo(q1 - 1) && k1 - 1 <= band_hi(q0)) return SA_TILE_FULL;
+        bool misses_band = k1 - 1 < band_lo(q0) || k0 > band_hi(q1 - 1);
+        if (misses_band && col_keys_in(k0, std::min(k1, key_limit(q1 - 1) + 1)) == 0)
+            return SA_TILE_EMPTY;
+    }
+    const int64_t cells = (q1 - q0) * (k1 - k0);
+    int64_t allowed = 0;
+    for (int64_t i = q0; i < q1; ++i) allowed += allowed_in(i, k0, k1);
+    return allowed == 0 ? SA_TILE_EMPTY : (allowed == cells ? SA_TILE_FULL : SA_TILE_PARTIAL);
+}
+
+HostPlan build_plan(const MaskRule& rule, int32_t bq, int32_t bk) {
+    HostPlan p;
+    const int64_t T = rule.T();
+    p.bq = bq;
+    p.bk = bk;
+    p.n_qb = static_cast<int32_t>((T + bq - 1) / bq);
+    p.n_kb = static_cast<int32_t>((T + bk - 1) / bk);
+    p.colbits.assign((T + 63) / 64, 0);
+    p.rowbits.assign((T + 31) / 32, 0);
+    for (int64_t j = 0; j < T; ++j) {
+        if (rule.col_key(j)) {
+            p.colkeys.push_back(static_cast<int32_t>(j));
+            p.colbits[j >> 6] |= uint64_t(1) << (j & 63);
+        }
+        if (rule.row_global(j)) p.rowbits[j >> 5] |= uint32_t(1) << (j & 31);
+    }
+    std::vector<int64_t> work(p.n_qb, 0);
+    p.run_ptr.push_back(0);
+    p.gseg.resize(4 * static_cast<size_t>(p.n_qb));
+    for (int32_t qb = 0; qb < p.n_qb; ++qb) {
+        const int64_t q0 = int64_t(qb) * bq, q1 = std::min<int64_t>(T, q0 + bq);
+        int64_t klo, khi;
+        if (rule.rows_global_in(q0, q1) > 0) {
+            klo = 0;
+            khi = rule.key_limit(q1 - 1);
+        } else {
+            klo = rule.band_lo(q0);
+            khi = rule.band_hi(q1 - 1);
+        }
+        const int64_t kb_lo = klo / bk, kb_hi = khi / bk + 1;
+        int64_t tiles = 0;
+        bool open = false;
+        for (int64_t kb = kb_lo; kb < kb_hi; ++kb) {
+            const int cls = rule.classify(q0, q1, kb * bk, (kb + 1) * bk);
+            if (cls == SA_TILE_EMPTY) {
+                open = false;
+                continue;
+            }
+            const bool need_mask = !(cls == SA_TILE_FULL && (kb + 1) * bk <= T);
+            const int32_t flag = need_mask ? int32_t(0x80000000u) : 0;
+            if (open && (p.runs.back() & int32_t(0x80000000u)) == flag &&
+                (p.runs.back() & 0x7fffffff) == kb) {
+                p.runs.back() = int32_t(kb + 1) | flag;
+            } else {
+                p.runs.push_back(static_cast<int32_t>(kb));
+                p.runs.push_back(int32_t(kb + 1) | flag);
+                open = true;
+            }
+            ++tiles;
+            p.masked_tiles += need_mask ? 1 : 0;
+        }
+        p.run_ptr.push_back(static_cast<int32_t>(p.runs.size() / 2));
+        // Gathered keys: strided/global keys outside [kb_lo*bk, kb_hi*bk)
+        // that some row of the block may read.  Below the block's band every
+        // such key precedes every row (causal holds); above it only bidir
+        // rows read, and they read all of them.
+        const int64_t limit = rule.key_limit(q1 - 1);
+        auto first_at_or_after = [&](int64_t key) {
+            return static_cast<int32_t>(
+                std::lower_bound(p.colkeys.begin(), p.colkeys.end(), key) - p.colkeys.begin());
+        };
+        const int32_t a0 = 0, a1 = first_at_or_after(kb_lo * bk);
+        int32_t b0 = first_at_or_after(kb_hi * bk), b1 = first_at_or_after(limit + 1);
+        if (b1 < b0) b1 = b0;
+        int32_t* g = &p.gseg[4 * static_cast<size_t>(qb)];
+        g[0] = a0;
+        g[1] = a1;
+        g[2] = b0;
+        g[3] = b1;
+        const int64_t nkeys = int64_t(a1 - a0) + (b1 - b0);
+        const int64_t gt = (nkeys + bk - 1) / bk;
+        p.inplace_tiles += tiles;
+        p.gathered_tiles += gt;
+        p.gathered_keys += nkeys;
+        work[qb] = tiles + gt;
+    }
+    p.qb_order.resize(p.n_qb);
+    std::iota(p.qb_order.begin(), p.qb_order.end(), 0);
+    std::stable_sort(p.qb_order.begin(), p.qb_order.end(),
+                     [&](int32_t x, int32_t y) { return work[x] > work[y]; });
+    return p;
+}
+
+}  // namespace sa

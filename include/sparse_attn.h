@@ -1,0 +1,176 @@
+/*
+ * sparse_attn.h -- C-ABI of the masked sparse attention library (forward),
+ * built for AMD MI355X (gfx950).  Library file: libsparse_attn.so.
+ *
+ * The operation ("Sparse attention", glossary.selfmadequant.com, section
+ * "Choose the available reads"): for every batch b, head h and query i,
+ *
+ *     O[b,h,i,:] = sum_{j in S_i} a_ij V[b,h,j,:],
+ *     a_ij = exp(Q_i.K_j / sqrt(d)) / sum_{l in S_i} exp(Q_i.K_l / sqrt(d)),
+ *
+ * a softmax renormalised over the allowed key set S_i only.  S_i comes from
+ * a mask spec (grammar below).  Pairs outside S_i are skipped tile by tile
+ * and never materialised ("Attention variants", sreshtalluri.github.io,
+ * section 5: the speed comes from never loading fully masked blocks).
+ *
+ * Mask rule.  allowed(i,j) = C and (L or St or Gl), with
+ *   C  = (j <= i) in causal mode, true in bidir mode
+ *   L  = causal: window == 0 or i - j < window   (the window counts the
+ *        query itself: "Attention variants" section 1; "Sparse attention",
+ *        octlm lab note, "A window, plus a few global columns")
+ *        bidir : no radius given or |i - j| <= radius ("Sparse Attention",
+ *        ai360xpert.com, "Local windows"; "Attention variants" section 3)
+ *   St = stride > 0 and j mod stride == phase (strided landmark columns;
+ *        phase 0 in the octlm lab note, stride-1 in "Attention variants")
+ *   Gl = i in G or j in G (global tokens read and are read by everyone;
+ *        in causal mode C still applies, "Attention variants" section 4).
+ *
+ * Mask-spec grammar (whitespace ignored; integers are decimal, >= 0,
+ * < 2^31; a key may appear once):
+ *   spec   := ('causal' | 'bidir') (';' clause)*
+ *   clause := 'window=' INT        causal only; 0 = unlimited (full causal)
+ *           | 'radius=' INT        bidir only; absent = unlimited
+ *           | 'stride=' INT        0 = no strided columns
+ *           | 'phase='  INT        needs stride > 0; 0 <= phase < stride
+ *           | 'global=' R (',' R)* R := INT | INT ':' INT  (half-open, a < b)
+ *
+ * Tensor layout.  Q, K, V, O are dense row-major [B][H][T][d] device arrays
+ * of one element type (bf16 for sparse_attn_fwd, fp32 for
+ * sparse_attn_fwd_f32), 16-byte aligned ("q, k, v: [batch, heads, n,
+ * d_head]", "Attention variants" section 4 "Use the library").  The scale
+ * is 1/sqrt(d).  O has the input's element type; bf16 output is rounded to
+ * nearest even from the fp32 accumulator.
+ *
+ * Ownership.  The caller owns Q, K, V and O; the library never allocates,
+ * frees or keeps them.  The library owns a per-device cache of execution
+ * plans (tile lists for one spec and T), built on first use and freed by
+ * sparse_attn_release_cache().  Calls are thread-safe.
+ *
+ * Streams.  Device work is enqueued on `stream` (a hipStream_t; NULL = the
+ * null stream) of the current device; the call returns after the enqueue.
+ * O is valid once the stream reaches that point.  Building a new plan makes
+ * one synchronous host-to-device copy before the launch.
+ *
+ * Errors.  Every call returns SA_OK or a negative status.  All checks run
+ * before anything is enqueued, so on error O is untouched.  No C++
+ * exception crosses this boundary.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define SA_OK 0
+#define SA_ERR_SPEC (-1)        /* mask spec does not parse */
+#define SA_ERR_RANGE (-2)       /* a global index >= T */
+#define SA_ERR_SHAPE (-3)       /* B, H or T < 1, T > SA_MAX_T, bad tile shape */
+#define SA_ERR_UNSUPPORTED (-4) /* d not in {16, 32, 64, 128}, unknown dtype */
+#define SA_ERR_NULL (-5)        /* a required pointer is NULL */
+#define SA_ERR_ALIAS (-6)       /* O overlaps Q, K or V */
+#define SA_ERR_HIP (-7)         /* a HIP runtime call or the launch failed */
+#define SA_ERR_ALIGN (-8)       /* a tensor pointer is not 16-byte aligned */
+#define SA_ERR_NOMEM (-9)       /* host or device allocation for a plan failed */
+
+/* tile classes written by sparse_attn_tile_map */
+#define SA_TILE_EMPTY 0   /* no allowed pair among the tile's in-range cells */
+#define SA_TILE_FULL 1    /* every in-range cell allowed */
+#define SA_TILE_PARTIAL 2 /* some, not all */
+
+/* element types */
+#define SA_DTYPE_BF16 0
+#define SA_DTYPE_F32 1
+
+#define SA_MAX_GLOBAL_RANGES 64
+#define SA_MAX_T (1 << 22)
+
+/* A parsed mask spec.  Global ranges are sorted, merged and half-open. */
+typedef struct sa_mask {
+    int32_t causal;     /* 1 = causal, 0 = bidir */
+    int32_t has_radius; /* bidir: 1 if radius= was given */
+    int64_t window;     /* causal: 0 = unlimited */
+    int64_t radius;     /* bidir: valid if has_radius */
+    int64_t stride;     /* 0 = none */
+    int64_t phase;
+    int32_t n_global;
+    int32_t reserved;
+    int64_t global_lo[SA_MAX_GLOBAL_RANGES];
+    int64_t global_hi[SA_MAX_GLOBAL_RANGES];
+} sa_mask;
+
+/* Summary of the plan the kernel runs for (spec, T, d, dtype).  Counts are
+ * per (batch, head). */
+typedef struct sa_plan_info {
+    int32_t bq, bk;              /* tile shape */
+    int32_t n_qb, n_kb;          /* query / key blocks */
+    int64_t inplace_tiles;       /* contiguous key tiles executed */
+    int64_t masked_tiles;        /* of those, tiles that evaluate the rule */
+    int64_t gathered_tiles;      /* tiles of gathered landmark/global keys */
+    int64_t gathered_keys;       /* keys staged through gathered tiles */
+    int64_t executed_cells;      /* bq * bk * (inplace + gathered tiles) */
+    int64_t allowed_cells;       /* E = sum_i |S_i| */
+} sa_plan_info;
+
+/*
+ * Forward pass, bf16 in and out.  Q, K, V, O: device pointers to
+ * [B][H][T][d] bf16 (raw 16-bit storage).  d in {16, 32, 64, 128}.
+ * mask_spec: NUL-terminated spec text.  stream: hipStream_t or NULL.
+ * Returns SA_OK or SA_ERR_{NULL, SHAPE, UNSUPPORTED, ALIGN, ALIAS, SPEC,
+ * RANGE, NOMEM, HIP}.
+ */
+int sparse_attn_fwd(const void* Q, const void* K, const void* V, void* O,
+                    int B, int H, int T, int d, const char* mask_spec,
+                    void* stream);
+
+/* Same as sparse_attn_fwd with fp32 tensors (fp32 MFMA, fp32 softmax). */
+int sparse_attn_fwd_f32(const void* Q, const void* K, const void* V, void* O,
+                        int B, int H, int T, int d, const char* mask_spec,
+                        void* stream);
+
+/* Parse mask_spec into *out (host only).  SA_ERR_SPEC on any grammar
+ * error, SA_ERR_NULL on NULL arguments. */
+int sparse_attn_parse(const char* mask_spec, sa_mask* out);
+
+/*
+ * Count allowed pairs for sequence length T (host only): *allowed_cells =
+ * E = sum_i |S_i| ("Sparse attention", glossary.selfmadequant.com, "Six
+ * tokens: count connections before claiming speed").  row_counts may be
+ * NULL, else receives |S_i| for i in [0, T).  SA_ERR_RANGE if a global
+ * index is >= T.
+ */
+int sparse_attn_count(const char* mask_spec, int T, int64_t* allowed_cells,
+                      int32_t* row_counts);
+
+/*
+ * Classify every (query block, key block) tile of a T x T grid cut into
+ * bq x bk tiles (host only).  map[qb * ceil(T/bk) + kb] receives
+ * SA_TILE_EMPTY / FULL / PARTIAL, judged over the tile's in-range cells
+ * (row and key < T).  Exact at any tile shape, not only the kernel's.
+ */
+int sparse_attn_tile_map(const char* mask_spec, int T, int bq, int bk,
+                         uint8_t* map);
+
+/* The tile shape the kernel uses for head dim d and dtype (SA_DTYPE_*). */
+int sparse_attn_tile_shape(int d, int dtype, int* bq, int* bk);
+
+/* Describe the plan the kernel would run (host only; builds no device
+ * state). */
+int sparse_attn_plan_info(const char* mask_spec, int T, int d, int dtype,
+                          sa_plan_info* info);
+
+/* Static text for a status code. */
+const char* sparse_attn_strerror(int status);
+
+/* Free every cached plan on every device.  The caller must make sure no
+ * launched kernel still uses them (synchronise first). */
+void sparse_attn_release_cache(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

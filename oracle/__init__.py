@@ -98,16 +98,17 @@ def parse_spec(spec: str) -> OracleMask:
             for item in val.split(","):
                 if ":" in item:
                     a, b = item.split(":", 1)
-                    if not (_INT.match(a) and _INT.match(b)) or int(a) >= int(b):
+                    if not (_INT.match(a) and _INT.match(b)) or int(a) >= int(b) \
+                            or int(b) >= 2 ** 31:
                         raise OracleSpecError(f"bad global range {item!r}")
                     ranges.append((int(a), int(b)))
                 else:
-                    if not _INT.match(item):
+                    if not _INT.match(item) or int(item) >= 2 ** 31:
                         raise OracleSpecError(f"bad global index {item!r}")
                     ranges.append((int(item), int(item) + 1))
             m.globals_ = ranges
             continue
-        if not _INT.match(val):
+        if not _INT.match(val) or int(val) >= 2 ** 31:
             raise OracleSpecError(f"bad integer {val!r}")
         v = int(val)
         if key == "window":
