@@ -30,7 +30,8 @@ METRIC = "allowed attention cells/s and effective TFLOP/s at 1 MI355X; % of bf16
 BF16_PEAK_TFLOPS = 2500.0
 F32_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "block_sparse_masked_spec_amd", "csrc", "fwd_kernel.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_masked_spec_amd", "csrc", f)
+               for f in ("fwd_kernel.hip", "fwd_bf16.hip", "internal.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = {
@@ -49,7 +50,10 @@ DEFAULT_WORKLOAD = "mistral32k_window4096"
 
 
 def kernel_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str):
@@ -73,11 +77,17 @@ def cpu_baseline(wl, specs, q, k, v, budget_s: float):
     rng = random.Random(0)
     all_rows = [(rng.randrange(B), rng.randrange(H), rng.randrange(T)) for _ in range(1 << 20)]
     spec = specs[0]
-    # calibrate on 256 rows, then size the sample to the budget
-    t0 = time.perf_counter()
-    _, _, n0 = oracle.forward_rows(spec, q, k, v, rows=all_rows[:256])
-    dt0 = time.perf_counter() - t0
-    n_rows = int(min(len(all_rows), max(256, 256 * budget_s / max(dt0, 1e-6))))
+    # calibrate on growing row counts until one run takes >= 1 s, then size
+    # the sample to the budget
+    n_cal = 256
+    while True:
+        t0 = time.perf_counter()
+        oracle.forward_rows(spec, q, k, v, rows=all_rows[:n_cal])
+        dt0 = time.perf_counter() - t0
+        if dt0 >= 1.0 or n_cal >= len(all_rows):
+            break
+        n_cal = min(len(all_rows), n_cal * 4)
+    n_rows = int(min(len(all_rows), max(256, n_cal * budget_s / max(dt0, 1e-6))))
     rows = all_rows[:n_rows]
     t0 = time.perf_counter()
     _, _, nset = oracle.forward_rows(spec, q, k, v, rows=rows)
@@ -103,6 +113,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (a "
+                         "known-size kernel for scaling HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -202,6 +215,15 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = {"read": n * 4, "write": n * 4}
+        del src, dst
     if args.cpu_budget > 0:
         q, k, v = host_sets[0]
         result["cpu_baseline"] = cpu_baseline(wl, specs, q, k, v, args.cpu_budget)

@@ -170,7 +170,9 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     a.colkeys = reinterpret_cast<const int32_t*>(base + dp.off_colkeys);
     a.colbits = reinterpret_cast<const uint64_t*>(base + dp.off_colbits);
     a.rowbits = reinterpret_cast<const uint32_t*>(base + dp.off_rowbits);
-    return sa::launch_fwd(dtype, d, a, BH * n_qb, stream);
+    int lrc = sa::launch_fwd_fast(dtype, d, a, BH * n_qb, stream);
+    if (lrc == SA_ERR_UNSUPPORTED) lrc = sa::launch_fwd(dtype, d, a, BH * n_qb, stream);
+    return lrc;
 }
 
 template <typename F>

@@ -1,0 +1,416 @@
+// Fast path of the fused forward kernel: bf16, head dim 64 or 128, gfx950.
+//
+// Same operation and tile plan as the generic kernel (fwd_kernel.hip): the
+// softmax over S_i only ("Sparse attention", glossary.selfmadequant.com,
+// "Choose the available reads"), live key tiles only ("Sparse and
+// sliding-window attention", getnybble.com, "Implementation").  What differs
+// is how a tile is fed to the matrix cores:
+//
+//   * workgroup = 2 wavefronts x 64 queries (two 32-query MFMA column
+//     groups per wave), so every K or V fragment read from LDS feeds two
+//     MFMAs -- half the LDS traffic per flop of a 32-query wave;
+//   * LDS holds each K and V tile "fragment-major": for every MFMA k-step,
+//     the 64 lanes' operand pieces are stored contiguously in lane order.
+//     Every fragment read is then lane_base + a compile-time offset and 32
+//     lanes read 512 consecutive bytes (no bank conflicts, one address
+//     register).  The permutation is done for free on the load side: the
+//     tiles are filled by direct global->LDS loads (16 bytes per lane, no
+//     register staging), each lane choosing its global source;
+//   * two LDS buffers: tile t+1 is loaded while tile t is computed;
+//   * V^T fragments come from transposed LDS reads (ds_read_b64_tr_b16):
+//     within each 16-lane group, output lane j element e is element j%4 of
+//     the 8-byte piece addressed by lane 4e + j/4;
+//   * the running max moves only when a score exceeds it by more than 2^8
+//     (log2 domain), so the accumulator rescale is almost never paid --
+//     exact either way, since every weight of a row uses the same reference;
+//   * row sums add the bf16-rounded weights with v_dot2 (the same values the
+//     PV MFMA consumes).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.hpp"
+
+namespace sa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+typedef __attribute__((address_space(3))) s16x4* lptr_s16x4_t;
+__device__ __forceinline__ gptr_t as_global(const void* p) { return (gptr_t)p; }
+__device__ __forceinline__ lptr_t as_lds(void* p) { return (lptr_t)p; }
+__device__ __forceinline__ lptr_s16x4_t as_lds_s16x4(const void* p) { return (lptr_s16x4_t)(void*)p; }
+
+// The plan is written before the launch and only read by the kernel, so it
+// can be read through the constant address space: uniform reads become
+// scalar loads, which do not share a wait counter with the tile loads.
+template <typename T>
+__device__ __forceinline__ T ldc(const T* p, int i) {
+    return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
+constexpr int kWaves2 = 2;
+constexpr int kThreads2 = kWaves2 * 64;
+constexpr float kLazyTau = 8.0f;  // log2-domain slack before the max moves
+static_assert(kBQ == kWaves2 * 64, "two waves of 64 queries per query block");
+static_assert(kBK == 64, "one column-bit word per key tile");
+
+__device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+template <int D>
+struct Lay {
+    static constexpr int TILE = kBK * D * 2;          // bytes per K or V tile
+    static constexpr int LOADS = TILE / 1024;         // 1 KiB wave-wide loads per tile
+    static constexpr int LOADS_PER_WAVE = LOADS / kWaves2;
+    static constexpr int NKS = D / 16;                // k-steps of S^T = K Q^T
+    static constexpr int NDB = D / 32;                // 32-row blocks of O^T
+    static_assert(LOADS == 2 * NKS && LOADS == 4 * NDB, "one 1 KiB block per k-step pair");
+};
+
+// K tile layout: 1 KiB block (b, ks) = b * NKS + ks holds, at byte lane*16,
+// the A fragment of lane (n = lane%32, h = lane/32) for key block b and
+// k-step ks: K[b*32 + swap23(n)][ks*16 + h*8 .. +8].  Rows enter the MFMA in
+// swap23 order so that a lane's 8 scores of one PV k-step are 8 consecutive
+// keys (register r of block b then holds key b*32 + (r/8)*16 + h*8 + r%8).
+//
+// V tile layout: 1 KiB block (kk, db) = kk * NDB + db holds two 512-byte
+// halves rd = 0, 1; transposed-read lane l reads 8 bytes at rd*512 + l*8:
+// V[kk*16 + h*8 + (l%16)/4 + 4*rd][db*32 + ((l/16)%2)*16 + (l%4)*4 .. +4].
+// After the transposed read, lane (n, h) holds V^T[db*32 + n][kk*16 + h*8 +
+// e] for e = 0..7 (rd = 0 gives e < 4) -- the A fragment of O^T += V^T P^T.
+
+// Where the next tile comes from: a run of in-place key tiles or a slice of
+// the gathered column keys.
+struct Cursor {
+    int run, run_end, kb, kb_end;
+    bool masked;
+    int gi, g_total;
+    __device__ bool done() const { return run >= run_end && gi >= g_total; }
+    __device__ bool inplace() const { return run < run_end; }
+};
+
+__device__ __forceinline__ void cursor_enter_run(Cursor& c, const FwdArgs& a) {
+    if (c.run < c.run_end) {
+        c.kb = ldc(a.runs, 2 * c.run);
+        const int w = ldc(a.runs, 2 * c.run + 1);
+        c.kb_end = w & 0x7fffffff;
+        c.masked = w < 0;
+    }
+}
+
+__device__ __forceinline__ void cursor_advance(Cursor& c, const FwdArgs& a) {
+    if (c.run < c.run_end) {
+        if (++c.kb == c.kb_end) {
+            ++c.run;
+            cursor_enter_run(c, a);
+        }
+    } else {
+        c.gi += kBK;
+    }
+}
+
+// Bits [0, n) set, n clamped to [0, 64].
+__device__ __forceinline__ uint64_t low_bits(int n) {
+    return n <= 0 ? 0ull : (n >= 64 ? ~0ull : ((1ull << n) - 1ull));
+}
+
+// Allowed keys of query qi among the 64 keys starting at k0, as a bit word:
+// (band OR column bits OR a global query row) AND key < T AND the causal cut.
+__device__ __forceinline__ uint64_t rule_word(const FwdArgs& a, int qi, int k0, bool rowg) {
+    uint64_t w = rowg ? ~0ull : ldc(a.colbits, k0 >> 6);
+    const long lo = long(qi) - a.band_back - k0;           // first band offset
+    const long hi = long(qi) + long(a.band_fwd) - k0 + 1;  // one past the last
+    if (!rowg && hi > 0 && lo < 64) {
+        const int l0 = lo < 0 ? 0 : int(lo), h0 = hi > 64 ? 64 : int(hi);
+        w |= low_bits(h0) & ~low_bits(l0);
+    }
+    w &= low_bits(a.T - k0);
+    if (a.causal) w &= low_bits(qi - k0 + 1);
+    return w;
+}
+
+// Tile row (key slot 0..63) that DMA instruction gi, lane `lane` copies, and
+// the element offset within that key's row.
+template <int D>
+__device__ __forceinline__ void k_piece(int gi, int lane, int* row, int* col) {
+    constexpr int NKS = Lay<D>::NKS;
+    *row = (gi / NKS) * 32 + swap23(lane & 31);
+    *col = (gi % NKS) * 16 + (lane >> 5) * 8;
+}
+template <int D>
+__device__ __forceinline__ void v_piece(int gi, int lane, int* row, int* col) {
+    constexpr int NDB = Lay<D>::NDB;
+    const int kk = gi / NDB, db = gi % NDB;
+    const int rd = lane >> 5, l0 = 2 * (lane & 31);
+    const int g = l0 >> 4, L = l0 & 15, h = l0 >> 5;
+    *row = kk * 16 + h * 8 + (L >> 2) + 4 * rd;
+    *col = db * 32 + (g & 1) * 16 + (L & 3) * 4;
+}
+
+// Issue the direct loads of one K tile and one V tile (this wave's share).
+// Slots that hold no key (past T, or unused gather slots) copy a valid row;
+// the mask gives them zero weight.  Gather keys are read before the first
+// load is issued, so no wait lands between the loads.
+template <int D>
+__device__ __forceinline__ void issue_tile(const Cursor& c, const FwdArgs& a, const __bf16* Kp,
+                                           const __bf16* Vp, char* kdst, char* vdst, int wave,
+                                           int lane, int T, int ga0, int gna, int gb0) {
+    using L = Lay<D>;
+    int kkey[L::LOADS_PER_WAVE], vkey[L::LOADS_PER_WAVE];
+    int kcol[L::LOADS_PER_WAVE], vcol[L::LOADS_PER_WAVE];
+    if (c.inplace()) {
+        const int k0 = c.kb * kBK;
+#pragma unroll
+        for (int i = 0; i < L::LOADS_PER_WAVE; ++i) {
+            const int gi = wave * L::LOADS_PER_WAVE + i;
+            int kr, vr;
+            k_piece<D>(gi, lane, &kr, &kcol[i]);
+            v_piece<D>(gi, lane, &vr, &vcol[i]);
+            kkey[i] = min(k0 + kr, T - 1);
+            vkey[i] = min(k0 + vr, T - 1);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < L::LOADS_PER_WAVE; ++i) {
+            const int gi = wave * L::LOADS_PER_WAVE + i;
+            int kr, vr;
+            k_piece<D>(gi, lane, &kr, &kcol[i]);
+            v_piece<D>(gi, lane, &vr, &vcol[i]);
+            const int ks = min(c.gi + kr, c.g_total - 1), vs = min(c.gi + vr, c.g_total - 1);
+            kkey[i] = a.colkeys[ks < gna ? ga0 + ks : gb0 + (ks - gna)];
+            vkey[i] = a.colkeys[vs < gna ? ga0 + vs : gb0 + (vs - gna)];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < L::LOADS_PER_WAVE; ++i) {
+        const int gi = wave * L::LOADS_PER_WAVE + i;
+        __builtin_amdgcn_global_load_lds(as_global(Kp + size_t(kkey[i]) * D + kcol[i]),
+                                         as_lds(kdst + gi * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(as_global(Vp + size_t(vkey[i]) * D + vcol[i]),
+                                         as_lds(vdst + gi * 1024), 16, 0, 0);
+    }
+}
+
+template <int D>
+struct Wave2 {
+    using L = Lay<D>;
+    bf16x8 qf[2][L::NKS];   // Q^T fragments of the two query groups
+    f32x16 acc[2][L::NDB];  // O^T accumulators
+    float m_run[2], l_run[2];
+
+    // One 64-key tile.  With `masked`, allowed[g] has bit k set iff key k of
+    // the tile is allowed for this lane's query of group g.
+    __device__ __forceinline__ void tile(const char* kt, const char* vt, const FwdArgs& a, int lane,
+                                         bool masked, const uint64_t (&allowed)[2]) {
+        const int h = lane >> 5;
+        f32x16 s[2][2];  // [query group][32-key block]
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) s[g][b] = f32x16{};
+        // S^T = K Q^T: one K fragment feeds both query groups.
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int ks = 0; ks < L::NKS; ++ks) {
+                const bf16x8 kf =
+                    *reinterpret_cast<const bf16x8*>(kt + (b * L::NKS + ks) * 1024 + lane * 16);
+                s[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0][ks], s[0][b], 0, 0, 0);
+                s[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[1][ks], s[1][b], 0, 0, 0);
+            }
+        bf16x8 pf[2][4];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            if (masked) {
+                // Register r of block b holds key b*32 + (r/8)*16 + h*8 + r%8.
+                const uint64_t mine = allowed[g] >> (h * 8);
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int bit = b * 32 + (r >> 3) * 16 + (r & 7);
+                        if (!((mine >> bit) & 1)) s[g][b][r] = -INFINITY;
+                    }
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[g][b][r]);
+            {
+                const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                                 __float_as_uint(mx), false, false);
+                mx = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+            }
+            const float ms = mx * a.scale_log2;
+            if (__any(ms > m_run[g] + kLazyTau)) {
+                const float m_new = fmaxf(m_run[g], ms);
+                const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+                m_run[g] = m_new;
+                l_run[g] *= alpha;
+#pragma unroll
+                for (int db = 0; db < L::NDB; ++db) acc[g][db] *= alpha;
+            }
+            const float mneg = -m_run[g];
+            bf16x2 ones;
+            ones[0] = static_cast<__bf16>(1.0f);
+            ones[1] = static_cast<__bf16>(1.0f);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(
+                        fmaf(s[g][kk >> 1][(kk & 1) * 8 + e], a.scale_log2, mneg));
+                    pf[g][kk][e] = static_cast<__bf16>(p);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    bf16x2 pair;
+                    pair[0] = pf[g][kk][e];
+                    pair[1] = pf[g][kk][e + 1];
+                    l_run[g] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_run[g], false);
+                }
+            }
+        }
+        // O^T += V^T P^T: one V^T fragment (two transposed reads) feeds both
+        // query groups.
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int db = 0; db < L::NDB; ++db) {
+                const char* blk = vt + (kk * L::NDB + db) * 1024 + lane * 8;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(blk));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(blk + 512));
+                const bf16x8 vf = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[0][kk], acc[0][db], 0, 0, 0);
+                acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[1][kk], acc[1][db], 0, 0, 0);
+            }
+    }
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads2) void sa_fwd_bf16_kernel(FwdArgs a) {
+    using L = Lay<D>;
+    // Two buffers as distinct objects, indexed statically (the loop below is
+    // unrolled by two), so the compiler can tell the prefetch into one from
+    // the reads of the other and keeps the prefetch in flight.
+    __shared__ __attribute__((aligned(1024))) char kbuf0[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char vbuf0[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char kbuf1[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char vbuf1[L::TILE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, h = lane >> 5;
+    const int bh = blockIdx.x % a.BH;
+    const int qb = ldc(a.qb_order, int(blockIdx.x / a.BH));
+    const int T = a.T;
+    const size_t base = size_t(bh) * size_t(T) * D;
+    const __bf16* Qp = static_cast<const __bf16*>(a.Q) + base;
+    const __bf16* Kp = static_cast<const __bf16*>(a.K) + base;
+    const __bf16* Vp = static_cast<const __bf16*>(a.V) + base;
+    __bf16* Op = static_cast<__bf16*>(a.O) + base;
+    const int q_base = qb * kBQ + wave * 64;
+
+    Wave2<D> st;
+    bool rowg[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const int qi = q_base + g * 32 + n;
+#pragma unroll
+        for (int ks = 0; ks < L::NKS; ++ks) {
+            st.qf[g][ks] = bf16x8{};
+            if (qi < T)
+                st.qf[g][ks] = *reinterpret_cast<const bf16x8*>(Qp + size_t(qi) * D + ks * 16 + h * 8);
+        }
+#pragma unroll
+        for (int db = 0; db < L::NDB; ++db) st.acc[g][db] = f32x16{};
+        st.m_run[g] = -1e30f;
+        st.l_run[g] = 0.f;
+        rowg[g] = qi < T && ((a.rowbits[qi >> 5] >> (qi & 31)) & 1u);
+    }
+
+    const int ga0 = ldc(a.gseg, 4 * qb), ga1 = ldc(a.gseg, 4 * qb + 1);
+    const int gb0 = ldc(a.gseg, 4 * qb + 2), gb1 = ldc(a.gseg, 4 * qb + 3);
+    const int gna = ga1 - ga0;
+    Cursor cur{ldc(a.run_ptr, qb), ldc(a.run_ptr, qb + 1), 0, 0, false, 0, gna + (gb1 - gb0)};
+    cursor_enter_run(cur, a);
+
+    auto run_tile = [&](const Cursor& c, const char* kt, const char* vt) {
+        const bool masked = !c.inplace() || c.masked;
+        uint64_t allowed[2] = {~0ull, ~0ull};
+        if (masked) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+                allowed[g] = c.inplace() ? rule_word(a, q_base + g * 32 + n, c.kb * kBK, rowg[g])
+                                         : low_bits(min(kBK, c.g_total - c.gi));
+        }
+        st.tile(kt, vt, a, lane, masked, allowed);
+    };
+
+    if (!cur.done()) issue_tile<D>(cur, a, Kp, Vp, kbuf0, vbuf0, wave, lane, T, ga0, gna, gb0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed
+    __syncthreads();                // ... and the other wave's
+    while (!cur.done()) {
+        Cursor nxt = cur;
+        cursor_advance(nxt, a);
+        if (!nxt.done()) issue_tile<D>(nxt, a, Kp, Vp, kbuf1, vbuf1, wave, lane, T, ga0, gna, gb0);
+        run_tile(cur, kbuf0, vbuf0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (nxt.done()) break;
+        cur = nxt;
+        cursor_advance(nxt, a);
+        if (!nxt.done()) issue_tile<D>(nxt, a, Kp, Vp, kbuf0, vbuf0, wave, lane, T, ga0, gna, gb0);
+        run_tile(cur, kbuf1, vbuf1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        cur = nxt;
+    }
+
+    // Epilogue: O = acc / l (both lane halves' sums).
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const int qi = q_base + g * 32 + n;
+        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.l_run[g]),
+                                                         __float_as_uint(st.l_run[g]), false, false);
+        const float lt = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+        const float inv = 1.f / lt;
+        if (qi < T) {
+#pragma unroll
+            for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int d0 = db * 32 + r4 * 8 + h * 4;
+                    bf16x4 q;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) q[e] = static_cast<__bf16>(st.acc[g][db][r4 * 4 + e] * inv);
+                    *reinterpret_cast<bf16x4*>(Op + size_t(qi) * D + d0) = q;
+                }
+        }
+    }
+}
+
+template <int D>
+int launch2(const FwdArgs& a, int64_t grid, void* stream) {
+    hipLaunchKernelGGL((sa_fwd_bf16_kernel<D>), dim3(static_cast<unsigned>(grid)), dim3(kThreads2),
+                       0, static_cast<hipStream_t>(stream), a);
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+}  // namespace
+
+// Returns SA_ERR_UNSUPPORTED when (dtype, d) has no fast path.
+int launch_fwd_fast(int dtype, int d, const FwdArgs& a, int64_t grid, void* stream) {
+    if (dtype != SA_DTYPE_BF16) return SA_ERR_UNSUPPORTED;
+    if (d == 128) return launch2<128>(a, grid, stream);
+    if (d == 64) return launch2<64>(a, grid, stream);
+    return SA_ERR_UNSUPPORTED;
+}
+
+}  // namespace sa

@@ -102,5 +102,7 @@ constexpr int kBK = 64;
 
 // Launch the fused forward kernel; returns SA_OK or SA_ERR_HIP.
 int launch_fwd(int dtype, int d, const FwdArgs& args, int64_t grid, void* stream);
+// The bf16 fast path (d = 64 or 128); SA_ERR_UNSUPPORTED for other shapes.
+int launch_fwd_fast(int dtype, int d, const FwdArgs& args, int64_t grid, void* stream);
 
 }  // namespace sa
