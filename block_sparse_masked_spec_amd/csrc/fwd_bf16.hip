@@ -6,9 +6,11 @@
 // sliding-window attention", getnybble.com, "Implementation").  What differs
 // is how a tile is fed to the matrix cores:
 //
-//   * workgroup = 2 wavefronts x 64 queries (two 32-query MFMA column
-//     groups per wave), so every K or V fragment read from LDS feeds two
-//     MFMAs -- half the LDS traffic per flop of a 32-query wave;
+//   * a workgroup of NW wavefronts covers 128 queries; each wave owns NG
+//     groups of 32 queries (one MFMA column block each).  With NG = 2 every
+//     K or V fragment read from LDS feeds two MFMAs; with NG = 1 a wave needs
+//     at most 256 registers, so two waves share each SIMD and one wave's
+//     softmax runs while the other's matrix products do;
 //   * LDS holds each K and V tile "fragment-major": for every MFMA k-step,
 //     the 64 lanes' operand pieces are stored contiguously in lane order.
 //     Every fragment read is then lane_base + a compile-time offset and 32
@@ -27,8 +29,10 @@
 //     PV MFMA consumes).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "internal.hpp"
+#include "kernel_common.hpp"
 
 namespace sa {
 namespace {
@@ -54,22 +58,20 @@ __device__ __forceinline__ T ldc(const T* p, int i) {
     return ((const __attribute__((address_space(4))) T*)p)[i];
 }
 
-constexpr int kWaves2 = 2;
-constexpr int kThreads2 = kWaves2 * 64;
 constexpr float kLazyTau = 8.0f;  // log2-domain slack before the max moves
-static_assert(kBQ == kWaves2 * 64, "two waves of 64 queries per query block");
 static_assert(kBK == 64, "one column-bit word per key tile");
 
 __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-template <int D>
+template <int D, int NW>
 struct Lay {
     static constexpr int TILE = kBK * D * 2;          // bytes per K or V tile
     static constexpr int LOADS = TILE / 1024;         // 1 KiB wave-wide loads per tile
-    static constexpr int LOADS_PER_WAVE = LOADS / kWaves2;
+    static constexpr int LOADS_PER_WAVE = LOADS / NW;
     static constexpr int NKS = D / 16;                // k-steps of S^T = K Q^T
     static constexpr int NDB = D / 32;                // 32-row blocks of O^T
     static_assert(LOADS == 2 * NKS && LOADS == 4 * NDB, "one 1 KiB block per k-step pair");
+    static_assert(LOADS % NW == 0, "loads split evenly over the waves");
 };
 
 // K tile layout: 1 KiB block (b, ks) = b * NKS + ks holds, at byte lane*16,
@@ -134,17 +136,17 @@ __device__ __forceinline__ uint64_t rule_word(const FwdArgs& a, int qi, int k0, 
     return w;
 }
 
-// Tile row (key slot 0..63) that DMA instruction gi, lane `lane` copies, and
+// Tile row (key slot 0..63) that load gi of a tile, lane `lane`, copies, and
 // the element offset within that key's row.
 template <int D>
 __device__ __forceinline__ void k_piece(int gi, int lane, int* row, int* col) {
-    constexpr int NKS = Lay<D>::NKS;
+    constexpr int NKS = D / 16;
     *row = (gi / NKS) * 32 + swap23(lane & 31);
     *col = (gi % NKS) * 16 + (lane >> 5) * 8;
 }
 template <int D>
 __device__ __forceinline__ void v_piece(int gi, int lane, int* row, int* col) {
-    constexpr int NDB = Lay<D>::NDB;
+    constexpr int NDB = D / 32;
     const int kk = gi / NDB, db = gi % NDB;
     const int rd = lane >> 5, l0 = 2 * (lane & 31);
     const int g = l0 >> 4, L = l0 & 15, h = l0 >> 5;
@@ -156,11 +158,11 @@ __device__ __forceinline__ void v_piece(int gi, int lane, int* row, int* col) {
 // Slots that hold no key (past T, or unused gather slots) copy a valid row;
 // the mask gives them zero weight.  Gather keys are read before the first
 // load is issued, so no wait lands between the loads.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void issue_tile(const Cursor& c, const FwdArgs& a, const __bf16* Kp,
                                            const __bf16* Vp, char* kdst, char* vdst, int wave,
                                            int lane, int T, int ga0, int gna, int gb0) {
-    using L = Lay<D>;
+    using L = Lay<D, NW>;
     int kkey[L::LOADS_PER_WAVE], vkey[L::LOADS_PER_WAVE];
     int kcol[L::LOADS_PER_WAVE], vcol[L::LOADS_PER_WAVE];
     if (c.inplace()) {
@@ -196,36 +198,37 @@ __device__ __forceinline__ void issue_tile(const Cursor& c, const FwdArgs& a, co
     }
 }
 
-template <int D>
-struct Wave2 {
-    using L = Lay<D>;
-    bf16x8 qf[2][L::NKS];   // Q^T fragments of the two query groups
-    f32x16 acc[2][L::NDB];  // O^T accumulators
-    float m_run[2], l_run[2];
+template <int D, int NG, int NW>
+struct WaveState {
+    using L = Lay<D, NW>;
+    bf16x8 qf[NG][L::NKS];   // Q^T fragments of the wave's query groups
+    f32x16 acc[NG][L::NDB];  // O^T accumulators
+    float m_run[NG], l_run[NG];
 
     // One 64-key tile.  With `masked`, allowed[g] has bit k set iff key k of
     // the tile is allowed for this lane's query of group g.
     __device__ __forceinline__ void tile(const char* kt, const char* vt, const FwdArgs& a, int lane,
-                                         bool masked, const uint64_t (&allowed)[2]) {
+                                         bool masked, const uint64_t (&allowed)[NG]) {
         const int h = lane >> 5;
-        f32x16 s[2][2];  // [query group][32-key block]
+        f32x16 s[NG][2];  // [query group][32-key block]
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
+        for (int g = 0; g < NG; ++g)
 #pragma unroll
             for (int b = 0; b < 2; ++b) s[g][b] = f32x16{};
-        // S^T = K Q^T: one K fragment feeds both query groups.
+        // S^T = K Q^T: one K fragment feeds every query group of the wave.
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int ks = 0; ks < L::NKS; ++ks) {
                 const bf16x8 kf =
                     *reinterpret_cast<const bf16x8*>(kt + (b * L::NKS + ks) * 1024 + lane * 16);
-                s[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0][ks], s[0][b], 0, 0, 0);
-                s[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[1][ks], s[1][b], 0, 0, 0);
-            }
-        bf16x8 pf[2][4];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
+                for (int g = 0; g < NG; ++g)
+                    s[g][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[g][ks], s[g][b], 0, 0, 0);
+            }
+        bf16x8 pf[NG][4];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
             if (masked) {
                 // Register r of block b holds key b*32 + (r/8)*16 + h*8 + r%8.
                 const uint64_t mine = allowed[g] >> (h * 8);
@@ -263,11 +266,9 @@ struct Wave2 {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(
-                        fmaf(s[g][kk >> 1][(kk & 1) * 8 + e], a.scale_log2, mneg));
-                    pf[g][kk][e] = static_cast<__bf16>(p);
-                }
+                for (int e = 0; e < 8; ++e)
+                    pf[g][kk][e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(
+                        fmaf(s[g][kk >> 1][(kk & 1) * 8 + e], a.scale_log2, mneg)));
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
                     bf16x2 pair;
@@ -277,8 +278,8 @@ struct Wave2 {
                 }
             }
         }
-        // O^T += V^T P^T: one V^T fragment (two transposed reads) feeds both
-        // query groups.
+        // O^T += V^T P^T: one V^T fragment (two transposed reads) feeds every
+        // query group of the wave.
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -288,15 +289,24 @@ struct Wave2 {
                 const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(blk + 512));
                 const bf16x8 vf = __builtin_bit_cast(
                     bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[0][kk], acc[0][db], 0, 0, 0);
-                acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[1][kk], acc[1][db], 0, 0, 0);
+#pragma unroll
+                for (int g = 0; g < NG; ++g)
+                    acc[g][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[g][kk], acc[g][db], 0, 0, 0);
             }
     }
 };
 
-template <int D>
-__global__ __launch_bounds__(kThreads2) void sa_fwd_bf16_kernel(FwdArgs a) {
-    using L = Lay<D>;
+// Waves per SIMD to ask the compiler for: two when a wave holds one query
+// group (fits in 256 registers), else one.
+template <int NG>
+struct Occupancy {
+    static constexpr int kWavesPerSimd = NG == 1 ? 2 : 1;
+};
+
+template <int D, int NG, int NW>
+__global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_bf16_kernel(FwdArgs a) {
+    static_assert(kBQ == NW * NG * 32, "waves x groups x 32 queries = one query block");
+    using L = Lay<D, NW>;
     // Two buffers as distinct objects, indexed statically (the loop below is
     // unrolled by two), so the compiler can tell the prefetch into one from
     // the reads of the other and keeps the prefetch in flight.
@@ -307,20 +317,22 @@ __global__ __launch_bounds__(kThreads2) void sa_fwd_bf16_kernel(FwdArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, h = lane >> 5;
-    const int bh = blockIdx.x % a.BH;
-    const int qb = ldc(a.qb_order, int(blockIdx.x / a.BH));
+    const int work = xcd_slice_index(blockIdx.x, gridDim.x);
+    const int n_qb = gridDim.x / a.BH;
+    const int bh = work / n_qb;
+    const int qb = ldc(a.qb_order, work % n_qb);
     const int T = a.T;
     const size_t base = size_t(bh) * size_t(T) * D;
     const __bf16* Qp = static_cast<const __bf16*>(a.Q) + base;
     const __bf16* Kp = static_cast<const __bf16*>(a.K) + base;
     const __bf16* Vp = static_cast<const __bf16*>(a.V) + base;
     __bf16* Op = static_cast<__bf16*>(a.O) + base;
-    const int q_base = qb * kBQ + wave * 64;
+    const int q_base = qb * kBQ + wave * NG * 32;
 
-    Wave2<D> st;
-    bool rowg[2];
+    WaveState<D, NG, NW> st;
+    bool rowg[NG];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < NG; ++g) {
         const int qi = q_base + g * 32 + n;
 #pragma unroll
         for (int ks = 0; ks < L::NKS; ++ks) {
@@ -343,30 +355,31 @@ __global__ __launch_bounds__(kThreads2) void sa_fwd_bf16_kernel(FwdArgs a) {
 
     auto run_tile = [&](const Cursor& c, const char* kt, const char* vt) {
         const bool masked = !c.inplace() || c.masked;
-        uint64_t allowed[2] = {~0ull, ~0ull};
-        if (masked) {
+        uint64_t allowed[NG];
 #pragma unroll
-            for (int g = 0; g < 2; ++g)
+        for (int g = 0; g < NG; ++g) {
+            allowed[g] = ~0ull;
+            if (masked)
                 allowed[g] = c.inplace() ? rule_word(a, q_base + g * 32 + n, c.kb * kBK, rowg[g])
                                          : low_bits(min(kBK, c.g_total - c.gi));
         }
         st.tile(kt, vt, a, lane, masked, allowed);
     };
 
-    if (!cur.done()) issue_tile<D>(cur, a, Kp, Vp, kbuf0, vbuf0, wave, lane, T, ga0, gna, gb0);
+    if (!cur.done()) issue_tile<D, NW>(cur, a, Kp, Vp, kbuf0, vbuf0, wave, lane, T, ga0, gna, gb0);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed
-    __syncthreads();                // ... and the other wave's
+    __syncthreads();                // ... and the other waves'
     while (!cur.done()) {
         Cursor nxt = cur;
         cursor_advance(nxt, a);
-        if (!nxt.done()) issue_tile<D>(nxt, a, Kp, Vp, kbuf1, vbuf1, wave, lane, T, ga0, gna, gb0);
+        if (!nxt.done()) issue_tile<D, NW>(nxt, a, Kp, Vp, kbuf1, vbuf1, wave, lane, T, ga0, gna, gb0);
         run_tile(cur, kbuf0, vbuf0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (nxt.done()) break;
         cur = nxt;
         cursor_advance(nxt, a);
-        if (!nxt.done()) issue_tile<D>(nxt, a, Kp, Vp, kbuf0, vbuf0, wave, lane, T, ga0, gna, gb0);
+        if (!nxt.done()) issue_tile<D, NW>(nxt, a, Kp, Vp, kbuf0, vbuf0, wave, lane, T, ga0, gna, gb0);
         run_tile(cur, kbuf1, vbuf1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -375,7 +388,7 @@ __global__ __launch_bounds__(kThreads2) void sa_fwd_bf16_kernel(FwdArgs a) {
 
     // Epilogue: O = acc / l (both lane halves' sums).
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < NG; ++g) {
         const int qi = q_base + g * 32 + n;
         const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.l_run[g]),
                                                          __float_as_uint(st.l_run[g]), false, false);
@@ -396,11 +409,21 @@ __global__ __launch_bounds__(kThreads2) void sa_fwd_bf16_kernel(FwdArgs a) {
     }
 }
 
-template <int D>
-int launch2(const FwdArgs& a, int64_t grid, void* stream) {
-    hipLaunchKernelGGL((sa_fwd_bf16_kernel<D>), dim3(static_cast<unsigned>(grid)), dim3(kThreads2),
-                       0, static_cast<hipStream_t>(stream), a);
+template <int D, int NG, int NW>
+int launch_t(const FwdArgs& a, int64_t grid, void* stream) {
+    hipLaunchKernelGGL((sa_fwd_bf16_kernel<D, NG, NW>), dim3(static_cast<unsigned>(grid)),
+                       dim3(NW * 64), 0, static_cast<hipStream_t>(stream), a);
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+// Which wave shape to use: SA_FAST_VARIANT=1 selects 64 queries per wave
+// (2 waves per workgroup), otherwise 32 queries per wave (4 waves).
+int fast_variant() {
+    static const int v = [] {
+        const char* e = getenv("SA_FAST_VARIANT");
+        return (e && e[0] == '1') ? 1 : 0;
+    }();
+    return v;
 }
 
 }  // namespace
@@ -408,8 +431,9 @@ int launch2(const FwdArgs& a, int64_t grid, void* stream) {
 // Returns SA_ERR_UNSUPPORTED when (dtype, d) has no fast path.
 int launch_fwd_fast(int dtype, int d, const FwdArgs& a, int64_t grid, void* stream) {
     if (dtype != SA_DTYPE_BF16) return SA_ERR_UNSUPPORTED;
-    if (d == 128) return launch2<128>(a, grid, stream);
-    if (d == 64) return launch2<64>(a, grid, stream);
+    const bool wide = fast_variant() == 1;
+    if (d == 128) return wide ? launch_t<128, 2, 2>(a, grid, stream) : launch_t<128, 1, 4>(a, grid, stream);
+    if (d == 64) return wide ? launch_t<64, 2, 2>(a, grid, stream) : launch_t<64, 1, 4>(a, grid, stream);
     return SA_ERR_UNSUPPORTED;
 }
 

@@ -31,6 +31,7 @@
 #include <type_traits>
 
 #include "internal.hpp"
+#include "kernel_common.hpp"
 
 namespace sa {
 namespace {
@@ -242,8 +243,10 @@ __global__ __launch_bounds__(kThreads) void sa_fwd_kernel(FwdArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, h = lane >> 5;
-    const int bh = blockIdx.x % a.BH;
-    const int qb = a.qb_order[blockIdx.x / a.BH];
+    const int work = xcd_slice_index(blockIdx.x, gridDim.x);
+    const int n_qb = gridDim.x / a.BH;
+    const int bh = work / n_qb;
+    const int qb = a.qb_order[work % n_qb];
     const int T = a.T;
     const size_t base = size_t(bh) * size_t(T) * D;
     const E* Qp = static_cast<const E*>(a.Q) + base;
