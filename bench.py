@@ -56,6 +56,11 @@ def kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
+def kernel_name(dtype: str, d: int) -> str:
+    """The kernel that runs the forward for this dtype and head size."""
+    return "sa_fwd_bf16_kernel" if dtype == "bf16" and d in (64, 128) else "sa_fwd_kernel"
+
+
 def load_traffic(workload: str):
     """HBM bytes per launch from the committed counter summary, or None."""
     try:
@@ -107,8 +112,8 @@ def cpu_baseline(wl, specs, q, k, v, budget_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
@@ -119,9 +124,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this "
-              "build (the path shards over heads and query blocks with no communication; see "
-              "the design notes), so nothing was run.", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported and nothing "
+              "was run (the forward shards over heads and query blocks with no communication, "
+              "so N GPUs each run this same kernel on H/N heads).", file=sys.stderr)
         return 2
 
     import torch
@@ -185,7 +190,7 @@ def main():
     roofline = {
         "bound": bound, "achieved": achieved, "peak": pk, "unit": unit,
         "frac": achieved / pk, "traffic": traffic,
-        "kernel": "sa_fwd_kernel", "ms_per_launch": ms_per_launch,
+        "kernel": kernel_name(dtype, d), "ms_per_launch": ms_per_launch,
         "algorithmic_flops_per_step": flops, "algorithmic_bytes_per_step": alg_bytes,
         "executed_over_allowed": executed / (E_total if E_total else 1),
     }
