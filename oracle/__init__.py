@@ -23,8 +23,9 @@ What it computes (fp64, no rounding of the result):
 Mask-spec text is parsed here by ``parse_spec`` (written independently of the
 product's parser).  Grammar: ``causal`` or ``bidir``, then ``;``-separated
 clauses ``window=W`` (causal; 0 = unlimited), ``radius=R`` (bidir),
-``stride=S``, ``phase=P`` (0 <= P < S), ``global=a,b:c,...`` (single indices
-or half-open ranges).
+``dilation=G`` (G >= 1: the local keys sit G apart, "Attention variants",
+section 6, dilated-mask exercise), ``stride=S``, ``phase=P`` (0 <= P < S),
+``global=a,b:c,...`` (single indices or half-open ranges).
 
 Pins (each in ``tests/test_oracle_pins.py``): the pages' printed cell counts
 and per-row key sets (``tests/golden/page_facts.json``), the closed form
@@ -64,6 +65,7 @@ class OracleMask:
     radius: int | None = None  # bidir: None = unlimited
     stride: int = 0
     phase: int = 0
+    dilation: int = 1          # local keys sit `dilation` apart
     globals_: list = field(default_factory=list)  # list of (lo, hi) half-open
 
     def global_set(self, T):
@@ -123,6 +125,10 @@ def parse_spec(spec: str) -> OracleMask:
             m.stride = v
         elif key == "phase":
             m.phase = v
+        elif key == "dilation":
+            if v < 1:
+                raise OracleSpecError("dilation must be >= 1")
+            m.dilation = v
         else:
             raise OracleSpecError(f"unknown key {key!r}")
     if "phase" in seen and m.stride == 0:
@@ -144,7 +150,7 @@ class _CMask(ctypes.Structure):
         ("stride", ctypes.c_int64),
         ("phase", ctypes.c_int64),
         ("n_global", ctypes.c_int32),
-        ("pad_", ctypes.c_int32),
+        ("dilation", ctypes.c_int32),
         ("global_lo", ctypes.POINTER(ctypes.c_int64)),
         ("global_hi", ctypes.POINTER(ctypes.c_int64)),
     ]
@@ -204,7 +210,7 @@ def _cmask(m: OracleMask):
         stride=m.stride,
         phase=m.phase,
         n_global=len(m.globals_),
-        pad_=0,
+        dilation=m.dilation,
         global_lo=lo.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
         global_hi=hi.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
     )
@@ -307,10 +313,12 @@ def dense_mask(spec, T: int) -> np.ndarray:
     from scratch": masks are unions of simple rules over index grids)."""
     m = _as_mask(spec)
     i, j = np.indices((T, T))
+    g_ = m.dilation
     if m.causal:
-        local = (i - j < m.window) if m.window else np.ones((T, T), bool)
+        local = (i - j < m.window * g_) if m.window else np.ones((T, T), bool)
     else:
-        local = (np.abs(i - j) <= m.radius) if m.radius is not None else np.ones((T, T), bool)
+        local = (np.abs(i - j) <= m.radius * g_) if m.radius is not None else np.ones((T, T), bool)
+    local &= (np.abs(i - j) % g_) == 0
     mask = local.copy()
     if m.stride:
         mask |= (j % m.stride) == m.phase

@@ -24,12 +24,18 @@
  *     strided columns at multiples of s (phase 0).
  *   - "Sparse Attention" (ai360xpert.com), "How It Actually Works": a
  *     non-causal local neighbourhood on either side, read as a radius r.
+ *   - "Attention variants", section 6 "Knowledge check" (the dilated-mask
+ *     exercise): a dilated window of w keys with dilation g reads the keys
+ *     at distances 0, g, 2g, ..., (w-1)g behind the query.  ("Sparse and
+ *     sliding-window attention", section "Dilated sliding window", describes
+ *     a different, symmetric variant; it is not the one used.)
  *
  * Mask rule used here (the plainest reading that covers every page):
  *   allowed(i,j) = C(i,j) and ( L(i,j) or St(j) or Gl(i,j) )
  *   C  : causal -> j <= i ; bidirectional -> always
- *   L  : causal -> window == 0 or i - j < window
- *        bidirectional -> no radius given or |i - j| <= radius
+ *   L  : with dilation g (default 1) and gap = i - j:
+ *        causal -> gap mod g == 0 and (window == 0 or gap < window * g)
+ *        bidirectional -> |gap| mod g == 0 and (no radius or |gap| <= radius * g)
  *   St : stride > 0 and j mod stride == phase
  *   Gl : i in G or j in G     (G = union of half-open index ranges)
  * In causal mode C is applied to the global term too, so a global token
@@ -51,7 +57,7 @@ typedef struct {
     int64_t stride;      /* 0 means no strided columns */
     int64_t phase;       /* 0 <= phase < stride */
     int32_t n_global;    /* number of half-open ranges in lo/hi */
-    int32_t pad_;
+    int32_t dilation;    /* >= 1; 1 = contiguous window */
     const int64_t* global_lo;
     const int64_t* global_hi;
 } oracle_mask;
@@ -68,10 +74,11 @@ int oracle_allowed(const oracle_mask* m, int64_t i, int64_t j) {
     if (!causal_ok) return 0;
     int local;
     if (m->causal) {
-        local = (m->window == 0) ? 1 : (i - j < m->window);
+        int64_t gap = i - j;
+        local = (gap % m->dilation == 0) && (m->window == 0 || gap < m->window * m->dilation);
     } else {
         int64_t dist = i > j ? i - j : j - i;
-        local = m->has_radius ? (dist <= m->radius) : 1;
+        local = (dist % m->dilation == 0) && (!m->has_radius || dist <= m->radius * m->dilation);
     }
     int strided = (m->stride > 0) && (j % m->stride == m->phase);
     int global = in_global(m, i) || in_global(m, j);

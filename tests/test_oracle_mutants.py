@@ -21,12 +21,12 @@ FACTS = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_f
 
 # (name, original text, planted text)
 MUTANTS = [
-    ("window_excludes_query", "(i - j < m->window)", "(i - j <= m->window)"),
-    ("window_sign_flipped", "(i - j < m->window)", "(j - i < m->window)"),
+    ("window_excludes_query", "gap < m->window * m->dilation", "gap <= m->window * m->dilation"),
+    ("window_sign_flipped", "int64_t gap = i - j;", "int64_t gap = j - i;"),
     ("causal_dropped", "int causal_ok = m->causal ? (j <= i) : 1;", "int causal_ok = 1;"),
     ("causal_strict", "int causal_ok = m->causal ? (j <= i) : 1;",
      "int causal_ok = m->causal ? (j < i) : 1;"),
-    ("radius_strict", "(dist <= m->radius)", "(dist < m->radius)"),
+    ("radius_strict", "dist <= m->radius * m->dilation", "dist < m->radius * m->dilation"),
     ("stride_phase_ignored", "(j % m->stride == m->phase)", "(j % m->stride == 0)"),
     ("stride_dropped", "return local || strided || global;", "return local || global;"),
     ("global_rows_dropped", "int global = in_global(m, i) || in_global(m, j);",
@@ -44,6 +44,10 @@ MUTANTS = [
     ("k_row_is_query_row", "const float* k = K + (bh * T + set[t]) * d;",
      "const float* k = K + (bh * T + i) * d;"),
     ("dot_uses_q_twice", "dot += (double)q[c] * (double)k[c];", "dot += (double)q[c] * (double)q[c];"),
+    ("dilation_grid_dropped", "(gap % m->dilation == 0) && ", ""),
+    ("dilation_grid_dropped_bidir", "(dist % m->dilation == 0) && ", ""),
+    ("dilation_span_unscaled", "gap < m->window * m->dilation", "gap < m->window"),
+    ("dilation_radius_unscaled", "dist <= m->radius * m->dilation", "dist <= m->radius"),
 ]
 
 
@@ -75,6 +79,11 @@ def _pins_pass() -> bool:
         s = torch.matmul(q.double(), k.double().transpose(-1, -2)) / math.sqrt(16)
         s = s.masked_fill(~torch.tril(torch.ones(33, 33, dtype=torch.bool)), float("-inf"))
         if not np.allclose(lse, torch.logsumexp(s, -1).numpy(), rtol=1e-10, atol=1e-10):
+            return False
+        # dilated windows: the exercise's n=16, w=4, g=2 count and a bidir row
+        if oracle.count("causal;window=4;dilation=2", 16) != sum(min(4, i // 2 + 1) for i in range(16)):
+            return False
+        if oracle.row_set("bidir;radius=3;dilation=4", 64, 30) != [18, 22, 26, 30, 34, 38, 42]:
             return False
         O1, _, _ = oracle.forward_rows("causal;window=1", q, k, v)
         if not np.array_equal(O1, v.double().numpy()):

@@ -354,3 +354,65 @@ def test_oracle_parser_rejects(bad):
 def test_oracle_parser_accepts_whitespace_and_ranges():
     m = oracle.parse_spec(" bidir ; radius = 2 ; global = 0 , 5:8 ")
     assert not m.causal and m.radius == 2 and m.globals_ == [(0, 1), (5, 8)]
+
+
+# ------------------------------------------------------------ dilated windows
+# "Attention variants", section 6 "Knowledge check", dilated-mask exercise:
+# each query reads w keys spaced g apart, the query itself, i-g, i-2g, ...
+
+@pytest.mark.parametrize("w,g,i", [(4, 2, 15), (4, 2, 6), (3, 5, 40), (1, 3, 9), (6, 1, 20)])
+def test_dilated_row_is_the_described_progression(w, g, i):
+    """The row set is the progression i, i-g, ..., i-(w-1)g cut at 0 -- the
+    exercise's own description, written as a list rather than as a rule."""
+    T = 48
+    expect = sorted(x for x in (i - t * g for t in range(w)) if x >= 0)
+    assert oracle.row_set(f"causal;window={w};dilation={g}", T, i) == expect
+
+
+@pytest.mark.parametrize("n,w,g", [(16, 4, 2), (33, 5, 3), (64, 8, 4), (20, 30, 2), (50, 1, 7)])
+def test_dilated_count_closed_form(n, w, g):
+    """Row i can step back floor(i/g) times, so |S_i| = min(w, floor(i/g)+1)
+    and E = sum_i min(w, floor(i/g) + 1).  The exercise's n=16, w=4, g=2
+    case gives 52."""
+    expect = sum(min(w, i // g + 1) for i in range(n))
+    assert oracle.count(f"causal;window={w};dilation={g}", n) == expect
+    if (n, w, g) == (16, 4, 2):
+        assert expect == 52
+
+
+def test_dilated_reach_of_the_longformer_example():
+    """"Sparse and sliding-window attention", section "Dilated sliding
+    window": with W = 512 and dilation 2 a token keeps 512 reads while its
+    reach doubles to about 1024 positions."""
+    spec = "causal;window=512;dilation=2"
+    S = oracle.row_set(spec, 6000, 5000)
+    assert len(S) == 512
+    assert 5000 - S[0] == 1022 and S[-1] == 5000  # span (w-1)*g + 1 = 1023 <= 1024
+
+
+def test_dilation_one_is_the_plain_window():
+    for spec in ["causal;window=5", "bidir;radius=3", "causal;window=0;stride=4"]:
+        a = spec + ";dilation=1"
+        assert oracle.count(spec, 40) == oracle.count(a, 40)
+        assert np.array_equal(oracle.tile_map(spec, 40, 8, 8), oracle.tile_map(a, 40, 8, 8))
+
+
+@pytest.mark.parametrize("base,g", [("causal;window=4", 2), ("causal;window=3", 3),
+                                    ("bidir;radius=2", 2), ("causal", 4)])
+def test_dilated_forward_is_plain_window_on_residue_classes(base, g):
+    """A dilated window links only positions of equal residue mod g, and on
+    each residue subsequence it is the plain window.  So the dilated output
+    equals the plain-window output of every subsequence Q[r::g], K[r::g],
+    V[r::g] -- computed through the oracle's pinned non-dilated path."""
+    T = 37
+    q, k, v = _rand(1, 2, T, 16, 21)
+    O, _, _ = oracle.forward_rows(f"{base};dilation={g}", q, k, v)
+    for r in range(g):
+        sub = [x[:, :, r::g].contiguous() for x in (q, k, v)]
+        Or, _, _ = oracle.forward_rows(base, *sub)
+        assert np.allclose(O[:, :, r::g], Or, rtol=1e-13, atol=1e-13)
+
+
+def test_dilated_bidir_rows_have_2r_plus_1_keys():
+    S = oracle.row_set("bidir;radius=3;dilation=4", 64, 30)
+    assert S == [18, 22, 26, 30, 34, 38, 42]
