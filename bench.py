@@ -43,6 +43,8 @@ WORKLOADS = {
                                         specs=["bidir;radius=256;stride=16;phase=0;global=0:128"]),
     "gemma_interleave_8k": dict(B=2, H=16, T=8192, d=128, dtype="bf16",
                                 specs=["causal;window=1024"] * 5 + ["causal"]),
+    "dilated16k_w512_g2": dict(B=1, H=16, T=16384, d=128, dtype="bf16",
+                               specs=["causal;window=512;dilation=2"]),
     "tiny_fp32_t16": dict(B=1, H=1, T=16, d=16, dtype="f32",
                           specs=["causal;window=2;stride=4;phase=3"]),
 }

@@ -53,7 +53,7 @@ class sa_mask(ctypes.Structure):
         ("causal", ctypes.c_int32), ("has_radius", ctypes.c_int32),
         ("window", ctypes.c_int64), ("radius", ctypes.c_int64),
         ("stride", ctypes.c_int64), ("phase", ctypes.c_int64),
-        ("n_global", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("n_global", ctypes.c_int32), ("dilation", ctypes.c_int32),
         ("global_lo", ctypes.c_int64 * SA_MAX_GLOBAL_RANGES),
         ("global_hi", ctypes.c_int64 * SA_MAX_GLOBAL_RANGES),
     ]

@@ -153,14 +153,12 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     a.T = T;
     a.BH = static_cast<int32_t>(BH);
     a.causal = m.causal;
-    // Band distances (same saturation as MaskRule::band_back/band_fwd).
-    if (m.causal) {
-        a.band_back = m.window == 0 ? INT32_MAX : static_cast<int32_t>(m.window - 1);
-        a.band_fwd = 0;
-    } else {
-        a.band_back = m.has_radius ? static_cast<int32_t>(m.radius) : INT32_MAX;
-        a.band_fwd = a.band_back;
-    }
+    // Band distances (as MaskRule::band_back/band_fwd) and the dilation grid.
+    a.band_back = sa::band_reach32(m);
+    a.band_fwd = m.causal ? 0 : a.band_back;
+    a.dil = m.dilation > 1 ? m.dilation : 1;
+    a.dil_pat = 0;
+    for (int x = 0; x < 64; x += a.dil) a.dil_pat |= uint64_t(1) << x;
     a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
     auto* base = static_cast<unsigned char*>(dp.base);
     a.qb_order = reinterpret_cast<const int32_t*>(base + dp.off_qb_order);

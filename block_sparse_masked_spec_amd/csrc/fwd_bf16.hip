@@ -123,13 +123,18 @@ __device__ __forceinline__ uint64_t low_bits(int n) {
 
 // Allowed keys of query qi among the 64 keys starting at k0, as a bit word:
 // (band OR column bits OR a global query row) AND key < T AND the causal cut.
-__device__ __forceinline__ uint64_t rule_word(const FwdArgs& a, int qi, int k0, bool rowg) {
+// The band is the distance range thinned to the dilation grid; qres = qi mod
+// g and k0res = k0 mod g (both 0 when g = 1).
+__device__ __forceinline__ uint64_t rule_word(const FwdArgs& a, int qi, int k0, bool rowg,
+                                              int qres, int k0res) {
     uint64_t w = rowg ? ~0ull : ldc(a.colbits, k0 >> 6);
     const long lo = long(qi) - a.band_back - k0;           // first band offset
     const long hi = long(qi) + long(a.band_fwd) - k0 + 1;  // one past the last
     if (!rowg && hi > 0 && lo < 64) {
         const int l0 = lo < 0 ? 0 : int(lo), h0 = hi > 64 ? 64 : int(hi);
-        w |= low_bits(h0) & ~low_bits(l0);
+        uint64_t band = low_bits(h0) & ~low_bits(l0);
+        if (a.dil != 1) band &= grid_word(a.dil_pat, a.dil, qres, k0res);
+        w |= band;
     }
     w &= low_bits(a.T - k0);
     if (a.causal) w &= low_bits(qi - k0 + 1);
@@ -331,6 +336,7 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
 
     WaveState<D, NG, NW> st;
     bool rowg[NG];
+    int qres[NG];  // query index mod the dilation
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const int qi = q_base + g * 32 + n;
@@ -345,6 +351,7 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
         st.m_run[g] = -1e30f;
         st.l_run[g] = 0.f;
         rowg[g] = qi < T && ((a.rowbits[qi >> 5] >> (qi & 31)) & 1u);
+        qres[g] = a.dil == 1 ? 0 : qi % a.dil;
     }
 
     const int ga0 = ldc(a.gseg, 4 * qb), ga1 = ldc(a.gseg, 4 * qb + 1);
@@ -356,11 +363,13 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
     auto run_tile = [&](const Cursor& c, const char* kt, const char* vt) {
         const bool masked = !c.inplace() || c.masked;
         uint64_t allowed[NG];
+        const int k0res = a.dil == 1 ? 0 : (c.kb * kBK) % a.dil;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             allowed[g] = ~0ull;
             if (masked)
-                allowed[g] = c.inplace() ? rule_word(a, q_base + g * 32 + n, c.kb * kBK, rowg[g])
+                allowed[g] = c.inplace() ? rule_word(a, q_base + g * 32 + n, c.kb * kBK, rowg[g],
+                                                     qres[g], k0res)
                                          : low_bits(min(kBK, c.g_total - c.gi));
         }
         st.tile(kt, vt, a, lane, masked, allowed);

@@ -14,6 +14,22 @@ namespace sa {
 int parse_mask_spec(const char* text, sa_mask* out);
 std::string canonical_spec(const sa_mask& m);
 
+// How far the local band reaches from the query, in keys: (w-1)g behind it
+// in causal mode, rg on each side in bidir mode (g = dilation); -1 when the
+// band is unlimited.
+inline int64_t band_reach(const sa_mask& m) {
+    const int64_t g = m.dilation > 1 ? m.dilation : 1;
+    if (m.causal) return m.window == 0 ? -1 : (m.window - 1) * g;
+    return m.has_radius ? m.radius * g : -1;
+}
+
+// band_reach as the kernels take it: INT32_MAX stands for unlimited (any
+// reach >= T is the same band).
+inline int32_t band_reach32(const sa_mask& m) {
+    const int64_t r = band_reach(m);
+    return r < 0 || r > INT32_MAX ? INT32_MAX : static_cast<int32_t>(r);
+}
+
 // The mask rule of sparse_attn.h for one sequence length, with prefix counts
 // of "column-rule" keys (strided or global) and of global rows so that the
 // number of allowed keys of any row inside any key range is O(1).
@@ -23,14 +39,16 @@ class MaskRule {
 
     int64_t T() const { return T_; }
     bool causal() const { return m_.causal != 0; }
+    int64_t dilation() const { return g_; }
     bool row_global(int64_t i) const { return rowpre_[i + 1] != rowpre_[i]; }
     bool col_key(int64_t j) const { return colpre_[j + 1] != colpre_[j]; }
     int64_t rows_global_in(int64_t a, int64_t b) const { return rowpre_[b] - rowpre_[a]; }
     int64_t col_keys_in(int64_t a, int64_t b) const {  // keys in [a, b)
         return a >= b ? 0 : colpre_[b] - colpre_[a];
     }
-    // Inclusive band [lo, hi] of row i, clipped to [0, T-1].  Both ends are
-    // non-decreasing in i.
+    // Inclusive extent [lo, hi] of row i's band, clipped to [0, T-1].  Both
+    // ends are non-decreasing in i.  With dilation g > 1 only the keys of the
+    // extent with j = i (mod g) are in the band.
     int64_t band_lo(int64_t i) const;
     int64_t band_hi(int64_t i) const;
     // Largest key a row may read at all (the causal limit).
@@ -40,16 +58,23 @@ class MaskRule {
     // SA_TILE_* for rows [q0, q1) x keys [k0, k1), judged on in-range cells.
     int classify(int64_t q0, int64_t q1, int64_t k0, int64_t k1) const;
     // Distance bounds of the band: key j is in row i's band iff
-    // i - j <= back and j - i <= fwd (saturated to INT32_MAX when unlimited).
+    // i - j <= back, j - i <= fwd (saturated to INT32_MAX when unlimited)
+    // and i - j = 0 (mod g).
     int32_t band_back() const;
     int32_t band_fwd() const;
     const std::vector<int64_t>& colpre() const { return colpre_; }
 
   private:
+    // Keys j in [a, b) with j = i (mod g), and the column keys among them.
+    int64_t on_grid(int64_t i, int64_t a, int64_t b) const;
+    int64_t col_keys_on_grid(int64_t i, int64_t a, int64_t b) const;
+
     sa_mask m_;
     int64_t T_;
+    int64_t g_;                    // dilation
     std::vector<int64_t> colpre_;  // T + 1 entries
     std::vector<int64_t> rowpre_;  // T + 1 entries
+    std::vector<int64_t> colres_;  // g > 1: column keys k <= j with k = j (mod g)
 };
 
 // Execution plan for one (spec, T, tile shape).  All counts per (b, h).
@@ -87,6 +112,8 @@ struct FwdArgs {
     int32_t causal;
     int32_t band_back;
     int32_t band_fwd;
+    int32_t dil;       // dilation g >= 1
+    uint64_t dil_pat;  // bits 0, g, 2g, ... below 64
     float scale_log2;  // log2(e) / sqrt(d)
     const int32_t* qb_order;
     const int32_t* run_ptr;

@@ -18,4 +18,13 @@ __device__ __forceinline__ int xcd_slice_index(int block, int total) {
     return die * q + min(die, r) + local;
 }
 
+// Dilated windows: bit x of the result is set iff key k0 + x is on query
+// qi's grid, qi - (k0 + x) = 0 (mod g).  pat has bits 0, g, 2g, ... below 64;
+// qres = qi mod g and k0res = k0 mod g.
+__device__ __forceinline__ uint64_t grid_word(uint64_t pat, int g, int qres, int k0res) {
+    int start = qres - k0res;
+    if (start < 0) start += g;
+    return start < 64 ? pat << start : 0ull;
+}
+
 }  // namespace sa

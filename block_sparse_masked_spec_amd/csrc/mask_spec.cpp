@@ -3,7 +3,8 @@
 // The spec names the rules of "Attention variants" (sreshtalluri.github.io),
 // section 1 "Intuition" and section 4 "Build it from scratch": a causal or
 // bidirectional base, a local window (causal, counting the query) or radius
-// (bidirectional), strided landmark columns with a phase, and global tokens.
+// (bidirectional), strided landmark columns with a phase, and global tokens;
+// plus a dilation of the local window (section 6, the dilated-mask exercise).
 // The grammar is documented in include/sparse_attn.h.
 #include "internal.hpp"
 
@@ -87,8 +88,9 @@ int parse_mask_spec(const char* text, sa_mask* out) {
     else
         return SA_ERR_SPEC;
 
+    m.dilation = 1;
     bool seen_window = false, seen_radius = false, seen_stride = false, seen_phase = false,
-         seen_global = false;
+         seen_global = false, seen_dilation = false;
     std::vector<std::pair<int64_t, int64_t>> ranges;
     while (c.eat(';')) {
         std::string key;
@@ -117,6 +119,10 @@ int parse_mask_spec(const char* text, sa_mask* out) {
             if (seen_phase) return SA_ERR_SPEC;
             seen_phase = true;
             m.phase = v;
+        } else if (key == "dilation") {
+            if (seen_dilation || v < 1) return SA_ERR_SPEC;
+            seen_dilation = true;
+            m.dilation = static_cast<int32_t>(v);
         } else {
             return SA_ERR_SPEC;
         }
@@ -148,6 +154,7 @@ std::string canonical_spec(const sa_mask& m) {
     std::string s = m.causal ? "causal" : "bidir";
     if (m.causal) s += ";window=" + std::to_string(m.window);
     if (!m.causal && m.has_radius) s += ";radius=" + std::to_string(m.radius);
+    if (m.dilation != 1) s += ";dilation=" + std::to_string(m.dilation);
     if (m.stride) s += ";stride=" + std::to_string(m.stride) + ";phase=" + std::to_string(m.phase);
     if (m.n_global) {
         s += ";global=";

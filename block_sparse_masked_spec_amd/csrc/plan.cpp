@@ -16,7 +16,8 @@
 
 namespace sa {
 
-MaskRule::MaskRule(const sa_mask& m, int64_t T) : m_(m), T_(T), colpre_(T + 1, 0), rowpre_(T + 1, 0) {
+MaskRule::MaskRule(const sa_mask& m, int64_t T)
+    : m_(m), T_(T), g_(m.dilation > 1 ? m.dilation : 1), colpre_(T + 1, 0), rowpre_(T + 1, 0) {
     std::vector<uint8_t> glob(T, 0);
     for (int k = 0; k < m.n_global; ++k)
         for (int64_t x = m.global_lo[k]; x < m.global_hi[k] && x < T; ++x) glob[x] = 1;
@@ -25,26 +26,43 @@ MaskRule::MaskRule(const sa_mask& m, int64_t T) : m_(m), T_(T), colpre_(T + 1, 0
         colpre_[j + 1] = colpre_[j] + ((strided || glob[j]) ? 1 : 0);
         rowpre_[j + 1] = rowpre_[j] + (glob[j] ? 1 : 0);
     }
+    if (g_ > 1) {
+        colres_.assign(T, 0);
+        for (int64_t j = 0; j < T; ++j)
+            colres_[j] = (j >= g_ ? colres_[j - g_] : 0) + (col_key(j) ? 1 : 0);
+    }
 }
 
 int64_t MaskRule::band_lo(int64_t i) const {
-    if (m_.causal) return m_.window == 0 ? 0 : std::max<int64_t>(0, i - m_.window + 1);
-    return m_.has_radius ? std::max<int64_t>(0, i - m_.radius) : 0;
+    const int64_t r = band_reach(m_);
+    return r < 0 ? 0 : std::max<int64_t>(0, i - r);
 }
 
 int64_t MaskRule::band_hi(int64_t i) const {
     if (m_.causal) return i;
-    return m_.has_radius ? std::min<int64_t>(T_ - 1, i + m_.radius) : T_ - 1;
+    const int64_t r = band_reach(m_);
+    return r < 0 ? T_ - 1 : std::min<int64_t>(T_ - 1, i + r);
 }
 
-int32_t MaskRule::band_back() const {
-    if (m_.causal) return m_.window == 0 ? INT32_MAX : static_cast<int32_t>(m_.window - 1);
-    return m_.has_radius ? static_cast<int32_t>(m_.radius) : INT32_MAX;
-}
+int32_t MaskRule::band_back() const { return band_reach32(m_); }
 
 int32_t MaskRule::band_fwd() const {
     if (m_.causal) return 0;
-    return m_.has_radius ? static_cast<int32_t>(m_.radius) : INT32_MAX;
+    return band_back();
+}
+
+int64_t MaskRule::on_grid(int64_t i, int64_t a, int64_t b) const {
+    if (a >= b) return 0;
+    const int64_t first = a + (((i - a) % g_) + g_) % g_;
+    return first >= b ? 0 : (b - 1 - first) / g_ + 1;
+}
+
+int64_t MaskRule::col_keys_on_grid(int64_t i, int64_t a, int64_t b) const {
+    if (g_ == 1) return col_keys_in(a, b);
+    const int64_t n = on_grid(i, a, b);
+    if (n == 0) return 0;
+    const int64_t first = a + (((i - a) % g_) + g_) % g_, last = first + (n - 1) * g_;
+    return colres_[last] - (first >= g_ ? colres_[first - g_] : 0);
 }
 
 int64_t MaskRule::allowed_in(int64_t i, int64_t a, int64_t b) const {
@@ -54,7 +72,7 @@ int64_t MaskRule::allowed_in(int64_t i, int64_t a, int64_t b) const {
     if (row_global(i)) return b - a;
     int64_t lo = std::max(a, band_lo(i)), hi = std::min(b, band_hi(i) + 1);
     if (lo >= hi) return col_keys_in(a, b);
-    return (hi - lo) + col_keys_in(a, b) - col_keys_in(lo, hi);
+    return on_grid(i, lo, hi) + col_keys_in(a, b) - col_keys_on_grid(i, lo, hi);
 }
 
 int MaskRule::classify(int64_t q0, int64_t q1, int64_t k0, int64_t k1) const {
@@ -64,7 +82,7 @@ int MaskRule::classify(int64_t q0, int64_t q1, int64_t k0, int64_t k1) const {
     if (rows_global_in(q0, q1) == 0) {
         // Band ends are monotone in i: the first row has the lowest upper
         // end, the last row the highest lower end.
-        if (k0 >= band_lo(q1 - 1) && k1 - 1 <= band_hi(q0)) return SA_TILE_FULL;
+        if (g_ == 1 && k0 >= band_lo(q1 - 1) && k1 - 1 <= band_hi(q0)) return SA_TILE_FULL;
         bool misses_band = k1 - 1 < band_lo(q0) || k0 > band_hi(q1 - 1);
         if (misses_band && col_keys_in(k0, std::min(k1, key_limit(q1 - 1) + 1)) == 0)
             return SA_TILE_EMPTY;

@@ -15,11 +15,15 @@
  *
  * Mask rule.  allowed(i,j) = C and (L or St or Gl), with
  *   C  = (j <= i) in causal mode, true in bidir mode
- *   L  = causal: window == 0 or i - j < window   (the window counts the
+ *   L  = with dilation g (default 1) and gap = i - j, gap mod g == 0 and
+ *        causal: window == 0 or gap < window * g   (the window counts the
  *        query itself: "Attention variants" section 1; "Sparse attention",
  *        octlm lab note, "A window, plus a few global columns")
- *        bidir : no radius given or |i - j| <= radius ("Sparse Attention",
- *        ai360xpert.com, "Local windows"; "Attention variants" section 3)
+ *        bidir : no radius given or |gap| <= radius * g ("Sparse
+ *        Attention", ai360xpert.com, "Local windows"; "Attention variants"
+ *        section 3)
+ *        With g > 1 the w window keys are i, i-g, ..., i-(w-1)g: the dilated
+ *        mask of "Attention variants" section 6 (knowledge check).
  *   St = stride > 0 and j mod stride == phase (strided landmark columns;
  *        phase 0 in the octlm lab note, stride-1 in "Attention variants")
  *   Gl = i in G or j in G (global tokens read and are read by everyone;
@@ -30,6 +34,7 @@
  *   spec   := ('causal' | 'bidir') (';' clause)*
  *   clause := 'window=' INT        causal only; 0 = unlimited (full causal)
  *           | 'radius=' INT        bidir only; absent = unlimited
+ *           | 'dilation=' INT      >= 1; local keys sit this far apart
  *           | 'stride=' INT        0 = no strided columns
  *           | 'phase='  INT        needs stride > 0; 0 <= phase < stride
  *           | 'global=' R (',' R)* R := INT | INT ':' INT  (half-open, a < b)
@@ -97,7 +102,7 @@ typedef struct sa_mask {
     int64_t stride;     /* 0 = none */
     int64_t phase;
     int32_t n_global;
-    int32_t reserved;
+    int32_t dilation;   /* >= 1 */
     int64_t global_lo[SA_MAX_GLOBAL_RANGES];
     int64_t global_hi[SA_MAX_GLOBAL_RANGES];
 } sa_mask;

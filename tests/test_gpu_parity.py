@@ -7,6 +7,7 @@ Tolerances (fixed in the test, read from the stated targets):
 Integer outputs (counts, tile maps) are checked bit-exact in the CPU suite.
 """
 import sys
+import zlib
 
 import numpy as np
 import pytest
@@ -90,6 +91,11 @@ SMALL_SPECS = [
     "bidir;radius=40;stride=16",
     "bidir;radius=5;global=0:3,150,299",
     "bidir;radius=2;stride=3;phase=2;global=64:130",
+    "causal;window=9;dilation=2",
+    "causal;window=20;dilation=3;stride=32;phase=1",
+    "bidir;radius=6;dilation=5;global=0:2",
+    "causal;window=0;dilation=7",
+    "causal;window=4;dilation=70",
 ]
 
 
@@ -98,7 +104,7 @@ SMALL_SPECS = [
 @pytest.mark.parametrize("spec", SMALL_SPECS)
 def test_small_ragged(gpu, spec, d, dtype):
     """T=300 spans 3 query blocks and 5 key tiles with ragged tails of both."""
-    full_check(gpu, spec, 2, 2, 300, d, dtype, seed=hash((spec, d)) % 1000)
+    full_check(gpu, spec, 2, 2, 300, d, dtype, seed=zlib.crc32(f"{spec}/{d}".encode()) % 1000)
 
 
 @pytest.mark.parametrize("T", [1, 2, 31, 63, 64, 65, 127, 128, 129, 191, 257])
@@ -171,6 +177,13 @@ def test_cfg_longformer_16k(gpu):
     global rows and columns included in the sample."""
     sampled_check(gpu, "bidir;radius=256;stride=16;phase=0;global=0:128", 1, 16, 16384, 64,
                   seed=0, extra=(5, 100, 127, 128, 129, 255, 256, 257, 16000))
+
+
+def test_cfg_dilated_16k(gpu):
+    """B=1, H=16, T=16384, d=128, causal dilated window: 512 keys spaced 2
+    apart (the W=512, dilation 2 example of the dilated sliding window)."""
+    sampled_check(gpu, "causal;window=512;dilation=2", 1, 16, 16384, 128, seed=0,
+                  extra=(1021, 1022, 1023, 1024, 1025, 4097))
 
 
 def test_cfg_gemma_interleave(gpu):

@@ -28,6 +28,9 @@ CONFIG_SPECS = [
     ("bidir;radius=256;stride=16;phase=0;global=0:128", 16384),
     ("causal;window=1024", 8192),
     ("causal", 8192),
+    ("causal;window=512;dilation=2", 4096),
+    ("bidir;radius=64;dilation=4;stride=128;phase=5;global=0:8", 2048),
+    ("causal;window=0;dilation=3;global=100:104", 1000),
 ]
 
 
@@ -53,8 +56,11 @@ def random_spec(rng: random.Random, T: int) -> str:
             else:
                 items.append(f"{a}:{min(T, a + rng.randint(1, 9))}")
         parts.append("global=" + ",".join(items))
-    rng.shuffle(parts[1:])
-    return ";".join(parts)
+    if rng.random() < 0.35:
+        parts.append(f"dilation={rng.choice([1, 2, 3, 5, 8, 70])}")
+    clauses = parts[1:]
+    rng.shuffle(clauses)  # clause order is free in the grammar
+    return ";".join(parts[:1] + clauses)
 
 
 # ------------------------------------------------------------------ exports
@@ -95,6 +101,7 @@ def test_plan_info_struct_size_matches_header():
     "causal;phase=1", "causal;stride=4;phase=4", "causal;window=-1", "causal;foo=1",
     "bidir;global=5:5", "bidir;global=a", "causal;window", "causal;stride=4;phase=x",
     "causal;window=99999999999", "causal;;window=2", "causal;window=2;", "causal window=2",
+    "causal;dilation=0", "causal;window=4;dilation=2;dilation=3", "bidir;dilation=",
 ])
 def test_parser_rejects(bad):
     with pytest.raises(sa.SparseAttnError) as e:
@@ -110,7 +117,9 @@ def test_parser_fields_and_normalisation():
     assert m.n_global == 3
     assert [(m.global_lo[k], m.global_hi[k]) for k in range(3)] == [(0, 1), (3, 4), (7, 12)]
     c = sa.sparse_attn_parse("causal;window=0;stride=4;phase=3")
-    assert (c.causal, c.window, c.stride, c.phase) == (1, 0, 4, 3)
+    assert (c.causal, c.window, c.stride, c.phase, c.dilation) == (1, 0, 4, 3, 1)
+    g = sa.sparse_attn_parse("causal;dilation=3;window=8")
+    assert (g.window, g.dilation) == (8, 3)
 
 
 def test_parser_null_arguments():
