@@ -142,16 +142,22 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     sa_mask m;
     int rc = parse_for(spec, T, &m);
     if (rc != SA_OK) return rc;
+    // Pure dilated windows run as `sub` interleaved plain windows.
+    const int sub = sa::residue_split(m, T, d, dtype) ? m.dilation : 1;
+    if (sub > 1) m.dilation = 1;
+    const int Ts = T / sub;
+    if (BH * sub * ((int64_t(Ts) + sa::kBQ - 1) / sa::kBQ) > INT32_MAX) return SA_ERR_SHAPE;
     DevicePlan dp;
-    rc = cache().get(m, T, &dp);
+    rc = cache().get(m, Ts, &dp);
     if (rc != SA_OK) return rc;
     sa::FwdArgs a;
     a.Q = Q;
     a.K = K;
     a.V = V;
     a.O = O;
-    a.T = T;
-    a.BH = static_cast<int32_t>(BH);
+    a.T = Ts;
+    a.BH = static_cast<int32_t>(BH * sub);
+    a.sub = sub;
     a.causal = m.causal;
     // Band distances (as MaskRule::band_back/band_fwd) and the dilation grid.
     a.band_back = sa::band_reach32(m);
@@ -168,8 +174,9 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     a.colkeys = reinterpret_cast<const int32_t*>(base + dp.off_colkeys);
     a.colbits = reinterpret_cast<const uint64_t*>(base + dp.off_colbits);
     a.rowbits = reinterpret_cast<const uint32_t*>(base + dp.off_rowbits);
-    int lrc = sa::launch_fwd_fast(dtype, d, a, BH * n_qb, stream);
-    if (lrc == SA_ERR_UNSUPPORTED) lrc = sa::launch_fwd(dtype, d, a, BH * n_qb, stream);
+    const int64_t grid = int64_t(a.BH) * dp.n_qb;
+    int lrc = sa::launch_fwd_fast(dtype, d, a, grid, stream);
+    if (lrc == SA_ERR_UNSUPPORTED && sub == 1) lrc = sa::launch_fwd(dtype, d, a, grid, stream);
     return lrc;
 }
 
@@ -256,17 +263,23 @@ SA_EXPORT int sparse_attn_plan_info(const char* mask_spec, int T, int d, int dty
         rc = parse_for(mask_spec, T, &m);
         if (rc != SA_OK) return rc;
         MaskRule rule(m, T);
-        HostPlan hp = sa::build_plan(rule, bq, bk);
+        // The plan the forward runs: for a residue split, one subsequence's.
+        const int sub = sa::residue_split(m, T, d, dtype) ? m.dilation : 1;
+        sa_mask mp = m;
+        if (sub > 1) mp.dilation = 1;
+        MaskRule prule(mp, T / sub);
+        HostPlan hp = sa::build_plan(prule, bq, bk);
         std::memset(info, 0, sizeof(*info));
         info->bq = bq;
         info->bk = bk;
         info->n_qb = hp.n_qb;
         info->n_kb = hp.n_kb;
-        info->inplace_tiles = hp.inplace_tiles;
-        info->masked_tiles = hp.masked_tiles;
-        info->gathered_tiles = hp.gathered_tiles;
-        info->gathered_keys = hp.gathered_keys;
-        info->executed_cells = int64_t(bq) * bk * (hp.inplace_tiles + hp.gathered_tiles);
+        info->subsequences = sub;
+        info->inplace_tiles = hp.inplace_tiles * sub;
+        info->masked_tiles = hp.masked_tiles * sub;
+        info->gathered_tiles = hp.gathered_tiles * sub;
+        info->gathered_keys = hp.gathered_keys * sub;
+        info->executed_cells = int64_t(bq) * bk * (hp.inplace_tiles + hp.gathered_tiles) * sub;
         int64_t total = 0;
         for (int64_t i = 0; i < T; ++i) total += rule.allowed_in(i, 0, T);
         info->allowed_cells = total;

@@ -164,9 +164,10 @@ __device__ __forceinline__ void v_piece(int gi, int lane, int* row, int* col) {
 // the mask gives them zero weight.  Gather keys are read before the first
 // load is issued, so no wait lands between the loads.
 template <int D, int NW>
-__device__ __forceinline__ void issue_tile(const Cursor& c, const FwdArgs& a, const __bf16* Kp,
-                                           const __bf16* Vp, char* kdst, char* vdst, int wave,
-                                           int lane, int T, int ga0, int gna, int gb0) {
+struct TileLoad {
+static __device__ __forceinline__ void issue(const Cursor& c, const FwdArgs& a, const __bf16* Kp,
+                                             const __bf16* Vp, char* kdst, char* vdst, int wave,
+                                             int lane, int T, int ga0, int gna, int gb0, size_t rs) {
     using L = Lay<D, NW>;
     int kkey[L::LOADS_PER_WAVE], vkey[L::LOADS_PER_WAVE];
     int kcol[L::LOADS_PER_WAVE], vcol[L::LOADS_PER_WAVE];
@@ -196,12 +197,13 @@ __device__ __forceinline__ void issue_tile(const Cursor& c, const FwdArgs& a, co
 #pragma unroll
     for (int i = 0; i < L::LOADS_PER_WAVE; ++i) {
         const int gi = wave * L::LOADS_PER_WAVE + i;
-        __builtin_amdgcn_global_load_lds(as_global(Kp + size_t(kkey[i]) * D + kcol[i]),
+        __builtin_amdgcn_global_load_lds(as_global(Kp + size_t(kkey[i]) * rs + kcol[i]),
                                          as_lds(kdst + gi * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(as_global(Vp + size_t(vkey[i]) * D + vcol[i]),
+        __builtin_amdgcn_global_load_lds(as_global(Vp + size_t(vkey[i]) * rs + vcol[i]),
                                          as_lds(vdst + gi * 1024), 16, 0, 0);
     }
 }
+};
 
 template <int D, int NG, int NW>
 struct WaveState {
@@ -308,7 +310,7 @@ struct Occupancy {
     static constexpr int kWavesPerSimd = NG == 1 ? 2 : 1;
 };
 
-template <int D, int NG, int NW>
+template <int D, int NG, int NW, bool SUB>
 __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_bf16_kernel(FwdArgs a) {
     static_assert(kBQ == NW * NG * 32, "waves x groups x 32 queries = one query block");
     using L = Lay<D, NW>;
@@ -327,7 +329,11 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
     const int bh = work / n_qb;
     const int qb = ldc(a.qb_order, work % n_qb);
     const int T = a.T;
-    const size_t base = size_t(bh) * size_t(T) * D;
+    // Row stride and base of this sequence; with SUB, sequence bh is residue
+    // class bh % sub of the full sequence bh / sub.
+    const size_t rs = SUB ? size_t(a.sub) * D : size_t(D);
+    const size_t base = SUB ? (size_t(bh / a.sub) * size_t(T) * a.sub + size_t(bh % a.sub)) * D
+                            : size_t(bh) * size_t(T) * D;
     const __bf16* Qp = static_cast<const __bf16*>(a.Q) + base;
     const __bf16* Kp = static_cast<const __bf16*>(a.K) + base;
     const __bf16* Vp = static_cast<const __bf16*>(a.V) + base;
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
         for (int ks = 0; ks < L::NKS; ++ks) {
             st.qf[g][ks] = bf16x8{};
             if (qi < T)
-                st.qf[g][ks] = *reinterpret_cast<const bf16x8*>(Qp + size_t(qi) * D + ks * 16 + h * 8);
+                st.qf[g][ks] = *reinterpret_cast<const bf16x8*>(Qp + size_t(qi) * rs + ks * 16 + h * 8);
         }
 #pragma unroll
         for (int db = 0; db < L::NDB; ++db) st.acc[g][db] = f32x16{};
@@ -375,20 +381,20 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
         st.tile(kt, vt, a, lane, masked, allowed);
     };
 
-    if (!cur.done()) issue_tile<D, NW>(cur, a, Kp, Vp, kbuf0, vbuf0, wave, lane, T, ga0, gna, gb0);
+    if (!cur.done()) TileLoad<D, NW>::issue(cur, a, Kp, Vp, kbuf0, vbuf0, wave, lane, T, ga0, gna, gb0, rs);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed
     __syncthreads();                // ... and the other waves'
     while (!cur.done()) {
         Cursor nxt = cur;
         cursor_advance(nxt, a);
-        if (!nxt.done()) issue_tile<D, NW>(nxt, a, Kp, Vp, kbuf1, vbuf1, wave, lane, T, ga0, gna, gb0);
+        if (!nxt.done()) TileLoad<D, NW>::issue(nxt, a, Kp, Vp, kbuf1, vbuf1, wave, lane, T, ga0, gna, gb0, rs);
         run_tile(cur, kbuf0, vbuf0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (nxt.done()) break;
         cur = nxt;
         cursor_advance(nxt, a);
-        if (!nxt.done()) issue_tile<D, NW>(nxt, a, Kp, Vp, kbuf0, vbuf0, wave, lane, T, ga0, gna, gb0);
+        if (!nxt.done()) TileLoad<D, NW>::issue(nxt, a, Kp, Vp, kbuf0, vbuf0, wave, lane, T, ga0, gna, gb0, rs);
         run_tile(cur, kbuf1, vbuf1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -412,15 +418,15 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
                     bf16x4 q;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) q[e] = static_cast<__bf16>(st.acc[g][db][r4 * 4 + e] * inv);
-                    *reinterpret_cast<bf16x4*>(Op + size_t(qi) * D + d0) = q;
+                    *reinterpret_cast<bf16x4*>(Op + size_t(qi) * rs + d0) = q;
                 }
         }
     }
 }
 
-template <int D, int NG, int NW>
+template <int D, int NG, int NW, bool SUB = false>
 int launch_t(const FwdArgs& a, int64_t grid, void* stream) {
-    hipLaunchKernelGGL((sa_fwd_bf16_kernel<D, NG, NW>), dim3(static_cast<unsigned>(grid)),
+    hipLaunchKernelGGL((sa_fwd_bf16_kernel<D, NG, NW, SUB>), dim3(static_cast<unsigned>(grid)),
                        dim3(NW * 64), 0, static_cast<hipStream_t>(stream), a);
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
@@ -441,6 +447,11 @@ int fast_variant() {
 int launch_fwd_fast(int dtype, int d, const FwdArgs& a, int64_t grid, void* stream) {
     if (dtype != SA_DTYPE_BF16) return SA_ERR_UNSUPPORTED;
     const bool wide = fast_variant() == 1;
+    if (a.sub > 1) {  // interleaved subsequences: strided rows
+        if (d == 128) return launch_t<128, 1, 4, true>(a, grid, stream);
+        if (d == 64) return launch_t<64, 1, 4, true>(a, grid, stream);
+        return SA_ERR_UNSUPPORTED;
+    }
     if (d == 128) return wide ? launch_t<128, 2, 2>(a, grid, stream) : launch_t<128, 1, 4>(a, grid, stream);
     if (d == 64) return wide ? launch_t<64, 2, 2>(a, grid, stream) : launch_t<64, 1, 4>(a, grid, stream);
     return SA_ERR_UNSUPPORTED;

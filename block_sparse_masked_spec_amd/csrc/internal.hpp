@@ -114,6 +114,10 @@ struct FwdArgs {
     int32_t band_fwd;
     int32_t dil;       // dilation g >= 1
     uint64_t dil_pat;  // bits 0, g, 2g, ... below 64
+    // Interleaved subsequences: with sub > 1 each of the BH sequences above is
+    // one residue class r of a sequence of T * sub rows (rows r, r + sub, ...),
+    // BH counts (b, h, r) triples, and rows sit sub * d elements apart.
+    int32_t sub;
     float scale_log2;  // log2(e) / sqrt(d)
     const int32_t* qb_order;
     const int32_t* run_ptr;
@@ -126,6 +130,15 @@ struct FwdArgs {
 
 constexpr int kBQ = 128;
 constexpr int kBK = 64;
+
+// A pure dilated window (no strided or global keys) links only rows of equal
+// residue mod g, and within a residue class it is the plain window.  When T
+// is a multiple of g the forward then runs as g interleaved plain-window
+// sequences of T/g rows each (the bf16 fast path only).
+inline bool residue_split(const sa_mask& m, int T, int d, int dtype) {
+    return m.dilation > 1 && m.stride == 0 && m.n_global == 0 && T % m.dilation == 0 &&
+           dtype == SA_DTYPE_BF16 && (d == 64 || d == 128);
+}
 
 // Launch the fused forward kernel; returns SA_OK or SA_ERR_HIP.
 int launch_fwd(int dtype, int d, const FwdArgs& args, int64_t grid, void* stream);

@@ -111,7 +111,13 @@ typedef struct sa_mask {
  * per (batch, head). */
 typedef struct sa_plan_info {
     int32_t bq, bk;              /* tile shape */
-    int32_t n_qb, n_kb;          /* query / key blocks */
+    int32_t n_qb, n_kb;          /* query / key blocks (of one subsequence) */
+    int32_t subsequences;        /* 1, or g when a pure dilated window (no
+                                    stride, no globals, T % g == 0, bf16,
+                                    d in {64, 128}) runs as g interleaved
+                                    plain windows of T/g rows; the tile
+                                    counts below are totals over all g */
+    int32_t reserved;
     int64_t inplace_tiles;       /* contiguous key tiles executed */
     int64_t masked_tiles;        /* of those, tiles that evaluate the rule */
     int64_t gathered_tiles;      /* tiles of gathered landmark/global keys */

@@ -96,6 +96,8 @@ SMALL_SPECS = [
     "bidir;radius=6;dilation=5;global=0:2",
     "causal;window=0;dilation=7",
     "causal;window=4;dilation=70",
+    "bidir;radius=7;dilation=3",
+    "causal;window=0;dilation=4",
 ]
 
 
@@ -112,6 +114,17 @@ def test_small_ragged(gpu, spec, d, dtype):
 def test_edge_lengths(gpu, T, dtype):
     for spec in ["causal;window=5;stride=7", "bidir;radius=9;global=0"]:
         full_check(gpu, spec, 1, 3, T, 64, dtype, seed=T)
+
+
+@pytest.mark.parametrize("T", [2, 6, 64, 130, 256, 512])
+@pytest.mark.parametrize("d", [64, 128])
+def test_dilated_interleaved_lengths(gpu, T, d):
+    """Pure dilated windows with T a multiple of g run as g interleaved
+    plain windows (strided rows); lengths cover one partial block, exact
+    blocks and ragged tails of the T/g-row subsequences."""
+    for spec in ["causal;window=5;dilation=2", "bidir;radius=3;dilation=2"]:
+        assert gpu.sparse_attn_plan_info(spec, T, d)["subsequences"] == 2
+        full_check(gpu, spec, 1, 3, T, d, "bf16", seed=T + d)
 
 
 def test_window_one_returns_values_exactly(gpu):
