@@ -31,7 +31,7 @@ BF16_PEAK_TFLOPS = 2500.0
 F32_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_masked_spec_amd", "csrc", f)
-               for f in ("fwd_kernel.hip", "fwd_bf16.hip", "internal.hpp")]
+               for f in ("fwd_kernel.hip", "fwd_bf16.hip", "decode.hip", "internal.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = {
@@ -45,6 +45,9 @@ WORKLOADS = {
                                 specs=["causal;window=1024"] * 5 + ["causal"]),
     "dilated16k_w512_g2": dict(B=1, H=16, T=16384, d=128, dtype="bf16",
                                specs=["causal;window=512;dilation=2"]),
+    "mistral_decode_b64_w4096": dict(kind="decode", B=64, H=32, Hkv=8, d=128, dtype="bf16",
+                                     n_new=1, C=4096, pos_range=(4096, 32768),
+                                     specs=["causal;window=4096"]),
     "tiny_fp32_t16": dict(B=1, H=1, T=16, d=16, dtype="f32",
                           specs=["causal;window=2;stride=4;phase=3"]),
 }
@@ -111,6 +114,87 @@ def cpu_baseline(wl, specs, q, k, v, budget_s: float):
     }
 
 
+def decode_bench(args, wl):
+    """Windowed decode: one step = one call decoding n_new tokens of each of B
+    sequences against ring-buffer caches of C rows (HBM-bound)."""
+    import numpy as np
+    import torch
+
+    from block_sparse_masked_spec_amd import binding as sa
+    from block_sparse_masked_spec_amd import inputs
+
+    B, H, Hkv, d, n_new, C = wl["B"], wl["H"], wl["Hkv"], wl["d"], wl["n_new"], wl["C"]
+    spec = wl["specs"][0]
+    rng = np.random.default_rng(args.seed)
+    pos = [int(x) for x in rng.integers(*wl["pos_range"], size=B)]
+    _, kc, vc = inputs.qkv(B, Hkv, C, d, "bf16", args.seed)
+    q = inputs.qkv(B, H, n_new, d, "bf16", args.seed + 1)[0]
+    qd, kd, vd = q.cuda(), kc.cuda(), vc.cuda()
+    od = torch.empty_like(qd)
+    posd = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    rows = sa.sparse_attn_decode_cache_rows(spec, n_new)
+    # allowed keys per new token: the window (all cache rows hold live positions here)
+    allowed = sum(min(rows - n_new + 1 if rows else p + 1, p + 1) for p in pos) * H * n_new
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sa.sparse_attn_decode(qd, kd, vd, od, posd, B, H, Hkv, n_new, C, d, spec, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    secs = ms / 1e3
+    # Algorithmic bytes: every allowed K and V row once, Q read, O written.
+    kv_rows = min(C, rows) if rows else C
+    alg_bytes = (2.0 * B * Hkv * kv_rows * d + 2.0 * B * H * n_new * d) * 2
+    flops = 4.0 * d * allowed
+    traffic = load_traffic(args.workload)
+    result = {
+        "metric": METRIC,
+        "value": allowed / secs,
+        "unit": "allowed cells/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid N(0,1) Q/K/V, no dataset)",
+        "config": {"workload": args.workload, "B": B, "H": H, "Hkv": Hkv, "d": d, "n_new": n_new,
+                   "cache_rows": C, "mask_specs": [spec], "allowed_cells_per_step": allowed,
+                   "parallelism": "single GPU"},
+        "effective_tflops": flops / secs / 1e12,
+        "wall_s_timed": wall,
+        "kernel_sha": kernel_sha(),
+        "roofline": {"bound": "hbm", "achieved": alg_bytes / secs / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": alg_bytes / secs / 1e9 / HBM_PEAK_GBS,
+                     "traffic": traffic, "kernel": "sa_decode_kernel", "ms_per_launch": ms,
+                     "algorithmic_bytes_per_step": alg_bytes},
+        "cpu_baseline": None,
+    }
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = {"read": n * 4, "write": n * 4}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +225,8 @@ def main():
         return 1
     sa.load()
     wl = WORKLOADS[args.workload]
+    if wl.get("kind") == "decode":
+        return decode_bench(args, wl)
     B, H, T, d, dtype, specs = wl["B"], wl["H"], wl["T"], wl["d"], wl["dtype"], wl["specs"]
     fwd = sa.sparse_attn_fwd if dtype == "bf16" else sa.sparse_attn_fwd_f32
 

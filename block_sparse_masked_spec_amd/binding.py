@@ -38,7 +38,8 @@ SA_MAX_GLOBAL_RANGES = 64
 EXPORTED = [
     "sparse_attn_fwd", "sparse_attn_fwd_f32", "sparse_attn_parse", "sparse_attn_count",
     "sparse_attn_tile_map", "sparse_attn_tile_shape", "sparse_attn_plan_info",
-    "sparse_attn_strerror", "sparse_attn_release_cache",
+    "sparse_attn_strerror", "sparse_attn_release_cache", "sparse_attn_decode",
+    "sparse_attn_decode_cache_rows",
 ]
 
 
@@ -100,6 +101,10 @@ def load():
     lib.sparse_attn_plan_info.restype = i32
     lib.sparse_attn_strerror.argtypes = [i32]
     lib.sparse_attn_strerror.restype = cs
+    lib.sparse_attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, cs, vp]
+    lib.sparse_attn_decode.restype = i32
+    lib.sparse_attn_decode_cache_rows.argtypes = [cs, i32, ctypes.POINTER(i64)]
+    lib.sparse_attn_decode_cache_rows.restype = i32
     lib.sparse_attn_release_cache.argtypes = []
     lib.sparse_attn_release_cache.restype = None
     _lib = lib
@@ -189,6 +194,23 @@ def sparse_attn_plan_info(mask_spec, T, d, dtype=SA_DTYPE_BF16) -> dict:
     _check(load().sparse_attn_plan_info(_spec(mask_spec), T, d, dtype, ctypes.byref(info)),
            "sparse_attn_plan_info")
     return {name: getattr(info, name) for name, _ in sa_plan_info._fields_}
+
+
+def sparse_attn_decode(Q, K_cache, V_cache, O, pos, B, H, Hkv, n_new, C, d, mask_spec,
+                       stream=None):
+    """bf16 windowed decode against ring-buffer caches; pos is a device
+    int32 tensor [B]; stream defaults to torch's current stream."""
+    return _check(load().sparse_attn_decode(_ptr(Q), _ptr(K_cache), _ptr(V_cache), _ptr(O),
+                                            _ptr(pos), B, H, Hkv, n_new, C, d, _spec(mask_spec),
+                                            _stream_handle(stream)),
+                  "sparse_attn_decode")
+
+
+def sparse_attn_decode_cache_rows(mask_spec, n_new=1) -> int:
+    rows = ctypes.c_int64(0)
+    _check(load().sparse_attn_decode_cache_rows(_spec(mask_spec), n_new, ctypes.byref(rows)),
+           "sparse_attn_decode_cache_rows")
+    return rows.value
 
 
 def sparse_attn_strerror(status):

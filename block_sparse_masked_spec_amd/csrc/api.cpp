@@ -3,6 +3,7 @@
 // include/sparse_attn.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -120,6 +121,63 @@ PlanCache& cache() {
     return *c;
 }
 
+// fp32 scratch for the key-split partials of decode, one buffer per (device,
+// stream) so that calls on different streams never share one.  A buffer only
+// grows; growing waits for the device first, since work queued earlier may
+// still read the old buffer.
+class Workspace {
+  public:
+    int get(size_t bytes, void* stream, float** out) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return SA_ERR_HIP;
+        const std::string key = std::to_string(dev) + "/" +
+                                std::to_string(reinterpret_cast<uintptr_t>(stream));
+        std::lock_guard<std::mutex> lock(mu_);
+        Entry& e = bufs_[key];
+        e.device = dev;
+        if (e.bytes < bytes) {
+            if (e.base) {
+                if (hipDeviceSynchronize() != hipSuccess) return SA_ERR_HIP;
+                (void)hipFree(e.base);
+                e.base = nullptr;
+                e.bytes = 0;
+            }
+            if (hipMalloc(&e.base, bytes) != hipSuccess) {
+                (void)hipGetLastError();
+                return SA_ERR_NOMEM;
+            }
+            e.bytes = bytes;
+        }
+        *out = static_cast<float*>(e.base);
+        return SA_OK;
+    }
+
+    void release() {
+        std::lock_guard<std::mutex> lock(mu_);
+        int cur = 0;
+        bool have_cur = hipGetDevice(&cur) == hipSuccess;
+        for (auto& kv : bufs_)
+            if (kv.second.base && hipSetDevice(kv.second.device) == hipSuccess)
+                (void)hipFree(kv.second.base);
+        if (have_cur) (void)hipSetDevice(cur);
+        bufs_.clear();
+    }
+
+  private:
+    struct Entry {
+        void* base = nullptr;
+        size_t bytes = 0;
+        int device = 0;
+    };
+    std::mutex mu_;
+    std::unordered_map<std::string, Entry> bufs_;
+};
+
+Workspace& workspace() {
+    static Workspace* w = new Workspace();
+    return *w;
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
     return x < y + nb && y < x + na;
@@ -192,6 +250,74 @@ int guarded(F&& f) {
 }
 
 }  // namespace
+
+// Decode: validation, key-split choice and launch.
+int decode_mask(const char* spec, int n_new, sa_mask* m, int64_t* min_rows) {
+    if (!spec) return SA_ERR_NULL;
+    int rc = sa::parse_mask_spec(spec, m);
+    if (rc != SA_OK) return rc;
+    // Landmark and global keys would need a cache of their own.
+    if (!m->causal || m->stride != 0 || m->n_global != 0) return SA_ERR_UNSUPPORTED;
+    const int64_t r = sa::band_reach(*m);
+    *min_rows = r < 0 ? 0 : r + n_new;
+    return SA_OK;
+}
+
+int decode(const void* Q, const void* K, const void* V, void* O, const int32_t* pos, int B,
+           int H, int Hkv, int n_new, int C, int d, const char* spec, void* stream) {
+    if (!Q || !K || !V || !O || !pos || !spec) return SA_ERR_NULL;
+    if (B < 1 || H < 1 || Hkv < 1 || n_new < 1 || C < 1 || C > SA_MAX_T || H % Hkv != 0 ||
+        B > 65535)
+        return SA_ERR_SHAPE;
+    if (!supported_d(d)) return SA_ERR_UNSUPPORTED;
+    for (const void* p : {Q, K, V, static_cast<const void*>(O)})
+        if (reinterpret_cast<uintptr_t>(p) % 16) return SA_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(pos) % 4) return SA_ERR_ALIGN;
+    sa_mask m;
+    int64_t min_rows = 0;
+    int rc = decode_mask(spec, n_new, &m, &min_rows);
+    if (rc != SA_OK) return rc;
+    if (min_rows > C) return SA_ERR_SHAPE;  // the cache cannot hold every allowed key
+    const int G = H / Hkv;
+    const int64_t nq_all = int64_t(G) * n_new;
+    const int64_t nqchunks = nq_all <= 8 ? 1 : (nq_all + 7) / 8;
+    if (int64_t(Hkv) * nqchunks > 65535) return SA_ERR_SHAPE;
+    const size_t qbytes = size_t(B) * H * n_new * d * 2, kvbytes = size_t(B) * Hkv * C * d * 2;
+    if (overlaps(O, qbytes, Q, qbytes) || overlaps(O, qbytes, K, kvbytes) ||
+        overlaps(O, qbytes, V, kvbytes))
+        return SA_ERR_ALIAS;
+
+    sa::DecodeArgs a;
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.O = O;
+    a.pos = pos;
+    a.part = nullptr;
+    a.B = B;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.G = G;
+    a.n_new = n_new;
+    a.C = C;
+    a.reach = sa::band_reach32(m);
+    a.dil = m.dilation > 1 ? m.dilation : 1;
+    a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
+    // Key splits: enough workgroups to cover the chip (about 2048), each
+    // with at least 256 keys.
+    int64_t keys = min_rows > 0 ? std::min<int64_t>(C, min_rows) : C;
+    if (n_new == 1 && a.dil > 1) keys = (keys + a.dil - 1) / a.dil;
+    const int64_t groups = int64_t(B) * Hkv * nqchunks;
+    int64_t nsplit = (2048 + groups - 1) / groups;
+    nsplit = std::max<int64_t>(1, std::min<int64_t>(nsplit, (keys + 255) / 256));
+    a.nsplit = static_cast<int32_t>(nsplit);
+    if (a.nsplit > 1) {
+        const size_t bytes = size_t(B) * H * n_new * size_t(a.nsplit) * (d + 2) * sizeof(float);
+        rc = workspace().get(bytes, stream, &a.part);
+        if (rc != SA_OK) return rc;
+    }
+    return sa::launch_decode(d, a, stream);
+}
 
 SA_EXPORT int sparse_attn_fwd(const void* Q, const void* K, const void* V, void* O, int B, int H,
                               int T, int d, const char* mask_spec, void* stream) {
@@ -303,9 +429,27 @@ SA_EXPORT const char* sparse_attn_strerror(int status) {
     }
 }
 
+SA_EXPORT int sparse_attn_decode(const void* Q, const void* K_cache, const void* V_cache, void* O,
+                                 const int32_t* pos, int B, int H, int Hkv, int n_new, int C,
+                                 int d, const char* mask_spec, void* stream) {
+    return guarded([&] {
+        return decode(Q, K_cache, V_cache, O, pos, B, H, Hkv, n_new, C, d, mask_spec, stream);
+    });
+}
+
+SA_EXPORT int sparse_attn_decode_cache_rows(const char* mask_spec, int n_new, int64_t* rows) {
+    return guarded([&] {
+        if (!rows) return SA_ERR_NULL;
+        if (n_new < 1) return SA_ERR_SHAPE;
+        sa_mask m;
+        return decode_mask(mask_spec, n_new, &m, rows);
+    });
+}
+
 SA_EXPORT void sparse_attn_release_cache(void) {
     try {
         cache().release();
+        workspace().release();
     } catch (...) {
     }
 }

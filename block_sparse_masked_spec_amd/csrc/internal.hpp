@@ -131,6 +131,24 @@ struct FwdArgs {
 constexpr int kBQ = 128;
 constexpr int kBK = 64;
 
+// Decode arguments (passed by value): n_new query tokens per sequence against
+// ring-buffer caches [B][Hkv][C][d]; position t lives in slot t mod C.
+struct DecodeArgs {
+    const void* Q;         // [B][H][n_new][d] bf16
+    const void* K;         // [B][Hkv][C][d] bf16
+    const void* V;         // [B][Hkv][C][d] bf16
+    void* O;               // [B][H][n_new][d] bf16
+    const int32_t* pos;    // [B] position of each sequence's last new token
+    float* part;           // nsplit > 1: [B*H*n_new][nsplit][d+2] fp32 (m, l, acc)
+    int32_t B, H, Hkv, G;  // G = H / Hkv query heads per KV head
+    int32_t n_new, C, nsplit;
+    int32_t reach;         // band reach (w-1)g, INT32_MAX = unlimited
+    int32_t dil;           // dilation g
+    float scale_log2;      // log2(e) / sqrt(d)
+};
+
+int launch_decode(int d, const DecodeArgs& args, void* stream);
+
 // A pure dilated window (no strided or global keys) links only rows of equal
 // residue mod g, and within a residue class it is the plain window.  When T
 // is a multiple of g the forward then runs as g interleaved plain-window

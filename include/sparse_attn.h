@@ -173,11 +173,56 @@ int sparse_attn_tile_shape(int d, int dtype, int* bq, int* bk);
 int sparse_attn_plan_info(const char* mask_spec, int T, int d, int dtype,
                           sa_plan_info* info);
 
+/*
+ * Windowed decode, bf16: n_new new query tokens per sequence against a
+ * ring-buffer KV cache that keeps only the last C positions ("Sparse and
+ * sliding-window attention", getnybble.com, section "Sliding window
+ * attention": the cache is capped at the window; "Attention variants",
+ * section 1 and section 3 "Worked example: KV cache for a long context").
+ *
+ *   Q        device [B][H][n_new][d]: the new tokens, at positions
+ *            pos[b]-n_new+1 .. pos[b] of sequence b.
+ *   K_cache, V_cache  device [B][Hkv][C][d]: position t of sequence b, KV
+ *            head k lives in row t mod C.  The new tokens' keys and values
+ *            must already be written.  H is a multiple of Hkv; query head h
+ *            reads KV head h / (H / Hkv) (grouped-query attention).
+ *   O        device [B][H][n_new][d], written.
+ *   pos      device int32 [B], read by the kernel (so a decode loop can
+ *            advance it on the device); pos[b] >= n_new - 1.
+ *   mask_spec  causal specs only, window (0 = unlimited) and dilation; a
+ *            spec with strided or global keys is SA_ERR_UNSUPPORTED (those
+ *            keys would need a cache of their own).
+ *
+ * Query i (absolute position) reads the live positions max(0, pos-C+1) ..
+ * pos that the mask rule allows.  That equals the forward's row i when C is
+ * at least sparse_attn_decode_cache_rows(spec, n_new) for a window, and when
+ * no position has left the cache (pos < C) for an unlimited window.  C below
+ * the window's need is SA_ERR_SHAPE.  A query with no live allowed key
+ * gets O = 0.
+ *
+ * Long caches are split over several workgroups whose partial results go
+ * through a library-owned fp32 workspace, one per (device, stream), grown on
+ * demand (growing synchronises the device) and freed by
+ * sparse_attn_release_cache.  Calls on one stream are ordered; calls on
+ * different streams never share a workspace.  Returns SA_OK or SA_ERR_{NULL,
+ * SHAPE, UNSUPPORTED, ALIGN, ALIAS, SPEC, NOMEM, HIP}; validation happens
+ * before any device work.
+ */
+int sparse_attn_decode(const void* Q, const void* K_cache, const void* V_cache, void* O,
+                       const int32_t* pos, int B, int H, int Hkv, int n_new, int C, int d,
+                       const char* mask_spec, void* stream);
+
+/* Cache rows decode needs for mask_spec and n_new new tokens (host only):
+ * (w-1)*g + n_new for a window w with dilation g -- for n_new = 1 and g = 1
+ * the last w positions; 0 when the window is unlimited (the cache must then
+ * hold the whole context).  SA_ERR_UNSUPPORTED for specs decode rejects. */
+int sparse_attn_decode_cache_rows(const char* mask_spec, int n_new, int64_t* rows);
+
 /* Static text for a status code. */
 const char* sparse_attn_strerror(int status);
 
-/* Free every cached plan on every device.  The caller must make sure no
- * launched kernel still uses them (synchronise first). */
+/* Free every cached plan and decode workspace on every device.  The caller
+ * must make sure no launched kernel still uses them (synchronise first). */
 void sparse_attn_release_cache(void);
 
 #ifdef __cplusplus

@@ -4,6 +4,7 @@ Counts and tile maps must equal the oracle's bit for bit; parse errors and
 argument errors must come back as the documented status codes.
 """
 import ctypes
+import json
 import os
 import random
 import re
@@ -16,6 +17,7 @@ from block_sparse_masked_spec_amd import binding as sa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+FACTS = json.load(open(os.path.join(ROOT, "tests", "golden", "page_facts.json")))
 
 CONFIG_SPECS = [
     ("causal;window=2;stride=4;phase=3", 16),
@@ -266,3 +268,68 @@ def test_forward_rejects_bad_arguments_before_any_device_work():
     assert fwd(A, Bp, C, O, 1, 1, 16, 16, b"causal;window=x", None) == sa.SA_ERR_SPEC
     assert fwd(A, Bp, C, O, 1, 1, 16, 16, b"causal;global=16", None) == sa.SA_ERR_RANGE
     assert lib.sparse_attn_fwd_f32(A, Bp, C, O, 1, 1, 16, 32, b"bidir;foo", None) == sa.SA_ERR_SPEC
+
+
+# ------------------------------------------------------------------- decode
+def test_decode_cache_rows_match_the_pages_kv_sizes():
+    """A sliding-window layer keeps its last w positions; with the pages'
+    kv_bytes = 2 * layers * n_kv * d_head * rows * bytes formula this gives
+    their printed cache sizes (tests/golden/page_facts.json, "kv_cache")."""
+    for f in FACTS["kv_cache"]:
+        rows = sa.sparse_attn_decode_cache_rows(f["spec"], 1)
+        if "rows" in f:
+            assert rows == f["rows"]
+            continue
+        b = 2 * f["layers"] * f["n_kv"] * f["d_head"] * rows * f["bytes_per"]
+        if "bytes" in f:
+            assert b == f["bytes"]
+        else:
+            assert round(b / 1e9, 2) == f["bytes_approx_gb"]
+
+
+def test_decode_cache_rows_rule():
+    rows = sa.sparse_attn_decode_cache_rows
+    assert rows("causal;window=16", 1) == 16
+    assert rows("causal;window=16", 4) == 19      # the oldest of 4 new tokens reaches 15 back
+    assert rows("causal;window=8;dilation=3", 1) == 22
+    assert rows("causal", 1) == 0                 # unlimited: the cache holds the whole context
+    lib = sa.load()
+    v = ctypes.c_int64(0)
+    for bad in [b"causal;stride=4", b"causal;window=4;global=0", b"bidir;radius=3"]:
+        assert lib.sparse_attn_decode_cache_rows(bad, 1, ctypes.byref(v)) == sa.SA_ERR_UNSUPPORTED
+    assert lib.sparse_attn_decode_cache_rows(b"causal", 0, ctypes.byref(v)) == sa.SA_ERR_SHAPE
+    assert lib.sparse_attn_decode_cache_rows(b"causal", 1, None) == sa.SA_ERR_NULL
+
+
+def test_decode_rejects_bad_arguments_before_any_device_work():
+    """As for the forward: every error below is found before the library
+    touches the device, so the fake pointers are never read."""
+    lib = sa.load()
+    Q, K, V, O, P = 0x10000, 0x200000, 0x400000, 0x600000, 0x800000
+    dec = lib.sparse_attn_decode
+    w = b"causal;window=16"
+    # (Q, K, V, O, pos, B, H, Hkv, n_new, C, d, spec)
+    ok = [Q, K, V, O, P, 2, 8, 2, 1, 16, 64, w]
+
+    def call(**kw):
+        args = list(ok)
+        names = ["Q", "K", "V", "O", "pos", "B", "H", "Hkv", "n_new", "C", "d", "spec"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return dec(*args, None)
+
+    assert call(Q=None) == sa.SA_ERR_NULL
+    assert call(pos=None) == sa.SA_ERR_NULL
+    assert call(spec=None) == sa.SA_ERR_NULL
+    assert call(B=0) == sa.SA_ERR_SHAPE
+    assert call(H=6, Hkv=4) == sa.SA_ERR_SHAPE          # H not a multiple of Hkv
+    assert call(n_new=0) == sa.SA_ERR_SHAPE
+    assert call(C=15) == sa.SA_ERR_SHAPE                # cannot hold the window
+    assert call(n_new=2) == sa.SA_ERR_SHAPE             # 2 new tokens need 17 rows
+    assert call(d=48) == sa.SA_ERR_UNSUPPORTED
+    assert call(spec=b"causal;window=16;stride=4") == sa.SA_ERR_UNSUPPORTED
+    assert call(spec=b"bidir;radius=4") == sa.SA_ERR_UNSUPPORTED
+    assert call(spec=b"causal;window=") == sa.SA_ERR_SPEC
+    assert call(Q=Q + 8) == sa.SA_ERR_ALIGN
+    assert call(pos=P + 2) == sa.SA_ERR_ALIGN
+    assert call(O=K + 64) == sa.SA_ERR_ALIAS
