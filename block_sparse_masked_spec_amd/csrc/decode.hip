@@ -37,7 +37,7 @@ __device__ __forceinline__ bf16x2 as_bf2(uint32_t w) { return __builtin_bit_cast
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
-constexpr int kUnroll = 4;  // keys per lane group in flight
+constexpr int kUnroll = 2;  // keys per lane group per chunk (two chunks in flight)
 
 // Sum over aligned groups of LPR lanes (LPR in {2, 4, 8, 16}); every lane of
 // the group receives the total.  Quad permutes swap neighbours (xor 1, xor
@@ -62,8 +62,8 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 __device__ __forceinline__ void merge_into(float& m, float& l, float* a, float m2, float l2,
                                            const float* a2, int n) {
     const float mn = fmaxf(m, m2);
-    const float s1 = mn == -INFINITY ? 0.f : exp2f(m - mn);
-    const float s2 = mn == -INFINITY ? 0.f : exp2f(m2 - mn);
+    const float s1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+    const float s2 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
     l = l * s1 + l2 * s2;
     for (int e = 0; e < n; ++e) a[e] = a[e] * s1 + a2[e] * s2;
     m = mn;
@@ -71,8 +71,10 @@ __device__ __forceinline__ void merge_into(float& m, float& l, float* a, float m
 
 template <int D, int NQ>
 __global__ __launch_bounds__(kDecThreads) void sa_decode_kernel(DecodeArgs a) {
-    constexpr int LPR = D / 8;         // lanes per key row
-    constexpr int GPW = 64 / LPR;      // key rows per wave step
+    constexpr int EPL = D >= 128 ? 16 : 8;  // elements of a key row per lane
+    constexpr int NW = EPL / 2;             // packed bf16 pairs per lane
+    constexpr int LPR = D / EPL;            // lanes per key row
+    constexpr int GPW = 64 / LPR;           // key rows per wave step
     constexpr int STEP = GPW * kDecWaves;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int grp = lane / LPR, sub = lane % LPR;
@@ -97,84 +99,132 @@ __global__ __launch_bounds__(kDecThreads) void sa_decode_kernel(DecodeArgs a) {
     const long nkeys = pos >= lo ? (long(pos) - lo) / ks + 1 : 0;
     const long chunk = (nkeys + a.nsplit - 1) / a.nsplit;
     const long kbeg = min(nkeys, long(split) * chunk), kend = min(nkeys, kbeg + chunk);
+    // With one new token every visited key is allowed (the range and the
+    // grid come from the rule); several new tokens need the rule per key.
+    const bool rule = a.n_new > 1;
 
     const size_t kvbase = (size_t(b) * a.Hkv + kvh) * size_t(a.C) * D;
-    const __bf16* Kc = static_cast<const __bf16*>(a.K) + kvbase + sub * 8;
-    const __bf16* Vc = static_cast<const __bf16*>(a.V) + kvbase + sub * 8;
+    const __bf16* Kc = static_cast<const __bf16*>(a.K) + kvbase + sub * EPL;
+    const __bf16* Vc = static_cast<const __bf16*>(a.V) + kvbase + sub * EPL;
     const int slot0 = int(lo % a.C);
 
     // Queries of this chunk: query q = gh * n_new + t reads with head
     // kvh * G + gh at position i_first + t.  Packed bf16 pairs of this lane's
     // d-slice.
-    uint32_t qw[NQ][4];
+    uint32_t qw[NQ][NW];
     int qpos[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         const int qq = q0 + min(q, nq - 1);
         const int gh = qq / a.n_new, t = qq % a.n_new;
         const int h = kvh * a.G + gh;
-        const uint4 w = *reinterpret_cast<const uint4*>(
-            static_cast<const __bf16*>(a.Q) + ((size_t(b) * a.H + h) * a.n_new + t) * D + sub * 8);
-        qw[q][0] = w.x;
-        qw[q][1] = w.y;
-        qw[q][2] = w.z;
-        qw[q][3] = w.w;
+        const uint4* src = reinterpret_cast<const uint4*>(
+            static_cast<const __bf16*>(a.Q) + ((size_t(b) * a.H + h) * a.n_new + t) * D + sub * EPL);
+#pragma unroll
+        for (int c = 0; c < NW / 4; ++c) {
+            const uint4 w = src[c];
+            qw[q][4 * c] = w.x;
+            qw[q][4 * c + 1] = w.y;
+            qw[q][4 * c + 2] = w.z;
+            qw[q][4 * c + 3] = w.w;
+        }
         qpos[q] = q < nq ? i_first + t : -1;  // -1: padding query, never allowed
     }
 
-    float m[NQ], l[NQ], acc[NQ][8];
+    float m[NQ], l[NQ], acc[NQ][EPL];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         m[q] = -INFINITY;
         l[q] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
+        for (int e = 0; e < EPL; ++e) acc[q][e] = 0.f;
     }
 
-    for (long k = kbeg + wave * GPW + grp; k < kend; k += long(STEP) * kUnroll) {
-        uint4 kr[kUnroll], vr[kUnroll];
+    // Chunks of kUnroll keys per lane group.  Software-pipelined: the loads
+    // of the next chunk are issued before the current one is scored, so each
+    // wave keeps memory requests in flight while it computes.
+    struct Chunk {
+        uint32_t kr[kUnroll][NW], vr[kUnroll][NW];
         int jj[kUnroll];
+    };
+    auto load = [&](Chunk& c, long k) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const long kk = min(k + long(u) * STEP, kend - 1);  // clamp: a valid row, masked below
-            jj[u] = k + long(u) * STEP < kend ? int(lo + kk * ks) : -1;
+            const long kk = min(k + long(u) * STEP, kend - 1);  // clamp: a valid row, dropped below
+            c.jj[u] = k + long(u) * STEP < kend ? int(lo + kk * ks) : -1;
             // kk * ks <= pos - lo < C, so one wrap at most
             int slot = slot0 + int(kk * ks);
             if (slot >= a.C) slot -= a.C;
-            kr[u] = *reinterpret_cast<const uint4*>(Kc + size_t(slot) * D);
-            vr[u] = *reinterpret_cast<const uint4*>(Vc + size_t(slot) * D);
+            const uint4* kp = reinterpret_cast<const uint4*>(Kc + size_t(slot) * D);
+            const uint4* vp = reinterpret_cast<const uint4*>(Vc + size_t(slot) * D);
+#pragma unroll
+            for (int x = 0; x < NW / 4; ++x) {
+                const uint4 kx = kp[x], vx = vp[x];
+                c.kr[u][4 * x] = kx.x; c.kr[u][4 * x + 1] = kx.y; c.kr[u][4 * x + 2] = kx.z; c.kr[u][4 * x + 3] = kx.w;
+                c.vr[u][4 * x] = vx.x; c.vr[u][4 * x + 1] = vx.y; c.vr[u][4 * x + 2] = vx.z; c.vr[u][4 * x + 3] = vx.w;
+            }
         }
+    };
+    auto compute = [&](const Chunk& c) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int j = jj[u];
-            float v[8];
-            v[0] = bf_lo(vr[u].x); v[1] = bf_hi(vr[u].x);
-            v[2] = bf_lo(vr[u].y); v[3] = bf_hi(vr[u].y);
-            v[4] = bf_lo(vr[u].z); v[5] = bf_hi(vr[u].z);
-            v[6] = bf_lo(vr[u].w); v[7] = bf_hi(vr[u].w);
+        for (int q = 0; q < NQ; ++q) {
+            float s[kUnroll];
+            float cmax = -INFINITY;
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-                float s = 0.f;
-                s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(qw[q][0]), as_bf2(kr[u].x), s, false);
-                s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(qw[q][1]), as_bf2(kr[u].y), s, false);
-                s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(qw[q][2]), as_bf2(kr[u].z), s, false);
-                s = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(qw[q][3]), as_bf2(kr[u].w), s, false);
-                s = group_sum<LPR>(s) * a.scale_log2;
-                // The rule: causal, inside the band, on the dilation grid.
-                const int i = qpos[q];
-                const int gap = i - j;
-                const bool ok = j >= 0 && i >= 0 && gap >= 0 && gap <= a.reach &&
-                                (a.dil == 1 || gap % a.dil == 0);
-                if (ok) {
-                    const float mn = fmaxf(m[q], s);
-                    const float sc = exp2f(m[q] - mn);  // 0 while m is -inf
-                    const float p = exp2f(s - mn);
-                    l[q] = l[q] * sc + p;
+            for (int u = 0; u < kUnroll; ++u) {
+                float x = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[q][e] = acc[q][e] * sc + p * v[e];
-                    m[q] = mn;
+                for (int w = 0; w < NW; ++w) x = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(qw[q][w]), as_bf2(c.kr[u][w]), x, false);
+                x = group_sum<LPR>(x) * a.scale_log2;
+                const int j = c.jj[u];
+                bool ok = j >= 0;
+                if (rule) {  // causal, inside the band, on the dilation grid
+                    const int gap = qpos[q] - j;
+                    ok = ok && qpos[q] >= 0 && gap >= 0 && gap <= a.reach && (a.dil == 1 || gap % a.dil == 0);
+                }
+                s[u] = ok ? x : -INFINITY;
+                cmax = fmaxf(cmax, s[u]);
+            }
+            if (cmax > m[q]) {  // the running max grows: rescale (rare once warm)
+                const float sc = __builtin_amdgcn_exp2f(m[q] - cmax);  // 0 while m is -inf
+                l[q] *= sc;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[q][e] *= sc;
+                m[q] = cmax;
+            }
+            // Weights are rounded to bf16 and both the sum and the values use
+            // the rounded ones.  acc[2w] += p * v_lo and acc[2w+1] += p * v_hi
+            // are dot products of (p, 0) and (0, p) with the packed pair.
+            if (m[q] == -INFINITY) continue;  // no allowed key yet
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const __bf16 pb = static_cast<__bf16>(__builtin_amdgcn_exp2f(s[u] - m[q]));
+                l[q] += static_cast<float>(pb);
+                const uint32_t pw = __builtin_bit_cast(uint16_t, pb);
+                const bf16x2 plo = as_bf2(pw), phi = as_bf2(pw << 16);
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    acc[q][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(plo, as_bf2(c.vr[u][w]), acc[q][2 * w], false);
+                    acc[q][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(phi, as_bf2(c.vr[u][w]), acc[q][2 * w + 1], false);
                 }
             }
+        }
+    };
+    const long stride = long(STEP) * kUnroll;
+    long k = kbeg + wave * GPW + grp;
+    if (k < kend) {
+        Chunk c0, c1;
+        load(c0, k);
+        for (;;) {
+            const long k1 = k + stride;
+            if (k1 < kend) load(c1, k1);
+            compute(c0);
+            if (k1 >= kend) break;
+            const long k2 = k1 + stride;
+            if (k2 < kend) load(c0, k2);
+            compute(c1);
+            if (k2 >= kend) break;
+            k = k2;
         }
     }
 
@@ -186,10 +236,10 @@ __global__ __launch_bounds__(kDecThreads) void sa_decode_kernel(DecodeArgs a) {
         for (int q = 0; q < NQ; ++q) {
             const float m2 = __shfl_xor(m[q], off);
             const float l2 = __shfl_xor(l[q], off);
-            float a2[8];
+            float a2[EPL];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a2[e] = __shfl_xor(acc[q][e], off);
-            merge_into(m[q], l[q], acc[q], m2, l2, a2, 8);
+            for (int e = 0; e < EPL; ++e) a2[e] = __shfl_xor(acc[q][e], off);
+            merge_into(m[q], l[q], acc[q], m2, l2, a2, EPL);
         }
     }
 
@@ -200,7 +250,7 @@ __global__ __launch_bounds__(kDecThreads) void sa_decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sa[wave][q][sub * 8 + e] = acc[q][e];
+            for (int e = 0; e < EPL; ++e) sa[wave][q][sub * EPL + e] = acc[q][e];
             if (sub == 0) {
                 sm[wave][q] = m[q];
                 sl[wave][q] = l[q];
