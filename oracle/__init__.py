@@ -25,7 +25,11 @@ product's parser).  Grammar: ``causal`` or ``bidir``, then ``;``-separated
 clauses ``window=W`` (causal; 0 = unlimited), ``radius=R`` (bidir),
 ``dilation=G`` (G >= 1: the local keys sit G apart, "Attention variants",
 section 6, dilated-mask exercise), ``stride=S``, ``phase=P`` (0 <= P < S),
-``global=a,b:c,...`` (single indices or half-open ranges).
+``global=a,b:c,...`` (single indices or half-open ranges).  Block mode
+(BigBird, "Sparse and sliding-window attention", section "Block-sparse
+attention: BigBird"): ``blocks;block=S`` then ``radius=`` (in blocks,
+default 0), ``random=R`` (random key blocks per query block, <= 4096),
+``seed=X``, ``stride``/``phase``/``global`` as above.
 
 Pins (each in ``tests/test_oracle_pins.py``): the pages' printed cell counts
 and per-row key sets (``tests/golden/page_facts.json``), the closed form
@@ -67,6 +71,9 @@ class OracleMask:
     phase: int = 0
     dilation: int = 1          # local keys sit `dilation` apart
     globals_: list = field(default_factory=list)  # list of (lo, hi) half-open
+    block: int = 0             # > 0: block mode (radius counts blocks)
+    random: int = 0            # block mode: random key blocks per query block
+    seed: int = 0              # block mode: random stream seed
 
     def global_set(self, T):
         s = set()
@@ -84,9 +91,10 @@ def parse_spec(spec: str) -> OracleMask:
         raise OracleSpecError("empty spec")
     parts = text.split(";")
     head = parts[0]
-    if head not in ("causal", "bidir"):
-        raise OracleSpecError(f"mode must be causal or bidir, got {head!r}")
+    if head not in ("causal", "bidir", "blocks"):
+        raise OracleSpecError(f"mode must be causal, bidir or blocks, got {head!r}")
     m = OracleMask(causal=(head == "causal"))
+    blocks = head == "blocks"
     seen = set()
     for clause in parts[1:]:
         if "=" not in clause:
@@ -113,6 +121,10 @@ def parse_spec(spec: str) -> OracleMask:
         if not _INT.match(val) or int(val) >= 2 ** 31:
             raise OracleSpecError(f"bad integer {val!r}")
         v = int(val)
+        if blocks and key in ("window", "dilation"):
+            raise OracleSpecError(f"{key} is not a block-mode clause")
+        if not blocks and key in ("block", "random", "seed"):
+            raise OracleSpecError(f"{key} needs block mode")
         if key == "window":
             if not m.causal:
                 raise OracleSpecError("window needs causal")
@@ -121,6 +133,16 @@ def parse_spec(spec: str) -> OracleMask:
             if m.causal:
                 raise OracleSpecError("radius needs bidir")
             m.radius = v
+        elif key == "block":
+            if v < 1:
+                raise OracleSpecError("block must be >= 1")
+            m.block = v
+        elif key == "random":
+            if v > 4096:
+                raise OracleSpecError("random must be <= 4096")
+            m.random = v
+        elif key == "seed":
+            m.seed = v
         elif key == "stride":
             m.stride = v
         elif key == "phase":
@@ -131,6 +153,11 @@ def parse_spec(spec: str) -> OracleMask:
             m.dilation = v
         else:
             raise OracleSpecError(f"unknown key {key!r}")
+    if blocks:
+        if m.block == 0:
+            raise OracleSpecError("block mode needs block=")
+        if m.radius is None:
+            m.radius = 0
     if "phase" in seen and m.stride == 0:
         raise OracleSpecError("phase needs stride > 0")
     if m.stride and not (0 <= m.phase < m.stride):
@@ -153,6 +180,9 @@ class _CMask(ctypes.Structure):
         ("dilation", ctypes.c_int32),
         ("global_lo", ctypes.POINTER(ctypes.c_int64)),
         ("global_hi", ctypes.POINTER(ctypes.c_int64)),
+        ("block", ctypes.c_int64),
+        ("n_random", ctypes.c_int64),
+        ("seed", ctypes.c_uint64),
     ]
 
 
@@ -180,6 +210,12 @@ def _load():
         P = ctypes.POINTER
         lib.oracle_allowed.argtypes = [P(_CMask), ctypes.c_int64, ctypes.c_int64]
         lib.oracle_allowed.restype = ctypes.c_int
+        lib.oracle_allowed_T.argtypes = [P(_CMask), ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+        lib.oracle_allowed_T.restype = ctypes.c_int
+        lib.oracle_splitmix64.argtypes = [P(ctypes.c_uint64)]
+        lib.oracle_splitmix64.restype = ctypes.c_uint64
+        lib.oracle_random_blocks.argtypes = [P(_CMask), ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+        lib.oracle_random_blocks.restype = ctypes.c_int64
         lib.oracle_row_set.argtypes = [P(_CMask), ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
         lib.oracle_row_set.restype = ctypes.c_int64
         lib.oracle_count.argtypes = [P(_CMask), ctypes.c_int64, ctypes.c_void_p]
@@ -213,6 +249,9 @@ def _cmask(m: OracleMask):
         dilation=m.dilation,
         global_lo=lo.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
         global_hi=hi.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        block=m.block,
+        n_random=m.random,
+        seed=m.seed,
     )
     return c, (lo, hi)
 
@@ -221,10 +260,30 @@ def _as_mask(spec_or_mask):
     return parse_spec(spec_or_mask) if isinstance(spec_or_mask, str) else spec_or_mask
 
 
-def allowed(spec, i: int, j: int) -> bool:
+def allowed(spec, i: int, j: int, T: int | None = None) -> bool:
+    """The rule for one pair; block mode needs T (it fixes the key blocks)."""
     m = _as_mask(spec)
     c, keep = _cmask(m)
+    if m.block:
+        if T is None:
+            raise ValueError("block mode needs T")
+        return bool(_load().oracle_allowed_T(ctypes.byref(c), T, i, j))
     return bool(_load().oracle_allowed(ctypes.byref(c), i, j))
+
+
+def splitmix64(state: int, n: int) -> list:
+    """The first n outputs of SplitMix64 started from `state`."""
+    st = ctypes.c_uint64(state)
+    return [int(_load().oracle_splitmix64(ctypes.byref(st))) for _ in range(n)]
+
+
+def random_blocks(spec, T: int, qb: int) -> list:
+    """Rand(qb): the random key blocks of query block qb, in draw order."""
+    m = _as_mask(spec)
+    c, keep = _cmask(m)
+    out = np.zeros(max(m.random, 1) + (-(-T // max(m.block, 1))), dtype=np.int64)
+    n = _load().oracle_random_blocks(ctypes.byref(c), T, qb, out.ctypes.data)
+    return out[:n].tolist()
 
 
 def row_set(spec, T: int, i: int) -> list:
@@ -313,6 +372,21 @@ def dense_mask(spec, T: int) -> np.ndarray:
     from scratch": masks are unions of simple rules over index grids)."""
     m = _as_mask(spec)
     i, j = np.indices((T, T))
+    if m.block:
+        qb, kb = i // m.block, j // m.block
+        mask = np.abs(qb - kb) <= m.radius
+        nqb = -(-T // m.block)
+        rnd = np.zeros((nqb, nqb), dtype=bool)
+        for b in range(nqb):
+            rnd[b, random_blocks(m, T, b)] = True
+        mask |= rnd[qb, kb]
+        if m.stride:
+            mask |= (j % m.stride) == m.phase
+        g = sorted(m.global_set(T))
+        if g:
+            mask[:, g] = True
+            mask[g, :] = True
+        return mask
     g_ = m.dilation
     if m.causal:
         local = (i - j < m.window * g_) if m.window else np.ones((T, T), bool)

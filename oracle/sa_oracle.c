@@ -42,6 +42,19 @@
  * never reads or is read from the future ("Attention variants", section 4:
  * global tokens in a decoder must stay causal).
  *
+ * Block mode (BigBird, "Sparse and sliding-window attention", section
+ * "Block-sparse attention: BigBird": a local window of 3 blocks, R random
+ * blocks and G global blocks, block size 64): with block size S, query block
+ * qb = i / S and key block kb = j / S,
+ *   allowed(i,j) = |qb - kb| <= radius  or  kb in Rand(qb)  or St(j)  or Gl(i,j)
+ * with no causal cut (the pattern is bidirectional).  Rand(qb) holds R
+ * distinct key blocks drawn uniformly from all ceil(T/S) blocks, local and
+ * global ones included ("from anywhere"): the draws are the SplitMix64
+ * stream (Steele, Lea and Flood, "Fast splittable pseudorandom number
+ * generators", OOPSLA 2014) started from state (seed << 32) | qb, each draw
+ * x giving block (x >> 32) mod nkb; repeats are skipped, at most 64*R draws
+ * are made, and with nkb <= R every block is taken.
+ *
  * Parity pins: see the module docstring of oracle/__init__.py.
  */
 #include <math.h>
@@ -60,7 +73,37 @@ typedef struct {
     int32_t dilation;    /* >= 1; 1 = contiguous window */
     const int64_t* global_lo;
     const int64_t* global_hi;
+    int64_t block;       /* > 0: block mode with this block size */
+    int64_t n_random;    /* block mode: random key blocks per query block */
+    uint64_t seed;       /* block mode: random stream seed */
 } oracle_mask;
+
+/* One SplitMix64 step: advance the state by the golden gamma, then mix. */
+uint64_t oracle_splitmix64(uint64_t* state) {
+    uint64_t z = (*state += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+/* Rand(qb) for T keys: writes up to n_random distinct key blocks (in draw
+ * order) to out, returns how many. */
+int64_t oracle_random_blocks(const oracle_mask* m, int64_t T, int64_t qb, int64_t* out) {
+    const int64_t nkb = (T + m->block - 1) / m->block;
+    int64_t n = 0;
+    if (nkb <= m->n_random) {
+        for (int64_t kb = 0; kb < nkb; ++kb) out[n++] = kb;
+        return n;
+    }
+    uint64_t state = (m->seed << 32) | (uint64_t)qb;
+    for (int64_t draw = 0; draw < 64 * m->n_random && n < m->n_random; ++draw) {
+        const int64_t kb = (int64_t)((oracle_splitmix64(&state) >> 32) % (uint64_t)nkb);
+        int seen = 0;
+        for (int64_t t = 0; t < n; ++t) seen |= (out[t] == kb);
+        if (!seen) out[n++] = kb;
+    }
+    return n;
+}
 
 static int in_global(const oracle_mask* m, int64_t x) {
     for (int32_t r = 0; r < m->n_global; ++r)
@@ -68,8 +111,33 @@ static int in_global(const oracle_mask* m, int64_t x) {
     return 0;
 }
 
-/* The rule of "allowed", one (query, key) pair at a time. */
-int oracle_allowed(const oracle_mask* m, int64_t i, int64_t j) {
+/* St(j) and Gl(i,j), shared by the token and block rules. */
+static int strided_col(const oracle_mask* m, int64_t j) {
+    return (m->stride > 0) && (j % m->stride == m->phase);
+}
+
+static int global_pair(const oracle_mask* m, int64_t i, int64_t j) {
+    int global = in_global(m, i) || in_global(m, j);
+    return global;
+}
+
+static int oracle_allowed_blocks(const oracle_mask* m, int64_t T, int64_t i, int64_t j) {
+    const int64_t qb = i / m->block, kb = j / m->block;
+    const int64_t dist = qb > kb ? qb - kb : kb - qb;
+    int local = dist <= m->radius;
+    int rnd = 0;
+    if (m->n_random > 0) {
+        int64_t blocks[4096];
+        const int64_t n = oracle_random_blocks(m, T, qb, blocks);
+        for (int64_t t = 0; t < n; ++t) rnd |= (blocks[t] == kb);
+    }
+    return local || rnd || strided_col(m, j) || global_pair(m, i, j);
+}
+
+/* The rule of "allowed", one (query, key) pair at a time (T matters only
+ * in block mode, where it fixes the number of key blocks). */
+int oracle_allowed_T(const oracle_mask* m, int64_t T, int64_t i, int64_t j) {
+    if (m->block > 0) return oracle_allowed_blocks(m, T, i, j);
     int causal_ok = m->causal ? (j <= i) : 1;
     if (!causal_ok) return 0;
     int local;
@@ -80,16 +148,21 @@ int oracle_allowed(const oracle_mask* m, int64_t i, int64_t j) {
         int64_t dist = i > j ? i - j : j - i;
         local = (dist % m->dilation == 0) && (!m->has_radius || dist <= m->radius * m->dilation);
     }
-    int strided = (m->stride > 0) && (j % m->stride == m->phase);
-    int global = in_global(m, i) || in_global(m, j);
+    int strided = strided_col(m, j);
+    int global = global_pair(m, i, j);
     return local || strided || global;
+}
+
+/* Token-level masks do not depend on T; block masks take T = 2^62. */
+int oracle_allowed(const oracle_mask* m, int64_t i, int64_t j) {
+    return oracle_allowed_T(m, (int64_t)1 << 62, i, j);
 }
 
 /* S_i written out as a sorted list by scanning every key; returns |S_i|. */
 int64_t oracle_row_set(const oracle_mask* m, int64_t T, int64_t i, int64_t* out) {
     int64_t n = 0;
     for (int64_t j = 0; j < T; ++j)
-        if (oracle_allowed(m, i, j)) {
+        if (oracle_allowed_T(m, T, i, j)) {
             if (out) out[n] = j;
             ++n;
         }
@@ -121,7 +194,7 @@ void oracle_tile_map(const oracle_mask* m, int64_t T, int64_t bq, int64_t bk,
             for (int64_t i = qb * bq; i < (qb + 1) * bq && i < T; ++i)
                 for (int64_t j = kb * bk; j < (kb + 1) * bk && j < T; ++j) {
                     ++cells;
-                    allowed += oracle_allowed(m, i, j);
+                    allowed += oracle_allowed_T(m, T, i, j);
                 }
             map[qb * nkb + kb] = allowed == 0 ? 0 : (allowed == cells ? 1 : 2);
         }

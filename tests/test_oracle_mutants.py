@@ -48,6 +48,14 @@ MUTANTS = [
     ("dilation_grid_dropped_bidir", "(dist % m->dilation == 0) && ", ""),
     ("dilation_span_unscaled", "gap < m->window * m->dilation", "gap < m->window"),
     ("dilation_radius_unscaled", "dist <= m->radius * m->dilation", "dist <= m->radius"),
+    ("block_random_ignored", "rnd |= (blocks[t] == kb);", "rnd |= 0;"),
+    ("block_radius_strict", "int local = dist <= m->radius;", "int local = dist < m->radius;"),
+    ("block_key_uses_query", "const int64_t qb = i / m->block, kb = j / m->block;",
+     "const int64_t qb = i / m->block, kb = i / m->block;"),
+    ("random_repeats_kept", "if (!seen) out[n++] = kb;", "out[n++] = kb;"),
+    ("splitmix_gamma", "0x9E3779B97F4A7C15ull", "0x9E3779B97F4A7C13ull"),
+    ("block_globals_dropped", "return local || rnd || strided_col(m, j) || global_pair(m, i, j);",
+     "return local || rnd || strided_col(m, j);"),
 ]
 
 
@@ -60,6 +68,9 @@ def _build_mutant(tmp_path, name, old, new):
     subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", str(path),
                     "-o", str(so), "-lm"], check=True)
     return str(so)
+
+
+SPLITMIX = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "splitmix64.json")))
 
 
 def _pins_pass() -> bool:
@@ -84,6 +95,23 @@ def _pins_pass() -> bool:
         if oracle.count("causal;window=4;dilation=2", 16) != sum(min(4, i // 2 + 1) for i in range(16)):
             return False
         if oracle.row_set("bidir;radius=3;dilation=4", 64, 30) != [18, 22, 26, 30, 34, 38, 42]:
+            return False
+        # block mode: the published SplitMix64 values, BigBird rows, block=1 identity
+        for seq in SPLITMIX["sequences"]:
+            if oracle.splitmix64(seq["seed"], 2) != [int(x) for x in seq["outputs"][:2]]:
+                return False
+        bb, T = "blocks;block=64;radius=1;random=3;seed=0;global=0:128", 4096
+        _, rows = oracle.count(bb, T, per_row=True)
+        if not (rows[:128] == T).all():
+            return False
+        for i in range(128, T, 97):
+            qb = i // 64
+            blocks = ({qb - 1, qb, qb + 1} & set(range(64))) | set(oracle.random_blocks(bb, T, qb)) | {0, 1}
+            if len(oracle.random_blocks(bb, T, qb)) != 3 or rows[i] != 64 * len(blocks):
+                return False
+        if any(len(set(oracle.random_blocks(bb, T, qb))) != 3 for qb in range(64)):
+            return False
+        if oracle.count("blocks;block=1;radius=2", 40) != oracle.count("bidir;radius=2", 40):
             return False
         O1, _, _ = oracle.forward_rows("causal;window=1", q, k, v)
         if not np.array_equal(O1, v.double().numpy()):

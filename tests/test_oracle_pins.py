@@ -416,3 +416,78 @@ def test_dilated_forward_is_plain_window_on_residue_classes(base, g):
 def test_dilated_bidir_rows_have_2r_plus_1_keys():
     S = oracle.row_set("bidir;radius=3;dilation=4", 64, 30)
     assert S == [18, 22, 26, 30, 34, 38, 42]
+
+
+# ------------------------------------------------------- block mode (BigBird)
+# "Sparse and sliding-window attention", section "Block-sparse attention:
+# BigBird": a local window of 3 blocks (W = 192 at block size 64), R = 3
+# random blocks and G = 2 global blocks; cost per token W + R + G.
+BIGBIRD = "blocks;block=64;radius=1;random=3;seed=0;global=0:128"
+SPLITMIX = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "splitmix64.json")))
+
+
+@pytest.mark.parametrize("seq", SPLITMIX["sequences"], ids=lambda s: str(s["seed"]))
+def test_splitmix64_published_outputs(seq):
+    assert oracle.splitmix64(seq["seed"], len(seq["outputs"])) == [int(x) for x in seq["outputs"]]
+
+
+def test_bigbird_cost_per_token_is_w_plus_r_plus_g():
+    """Every non-global row reads its 3 local blocks, its random blocks and
+    the 2 global blocks: 192 + 192 + 128 = 512 keys when those blocks are
+    all different, fewer by 64 per coinciding block; global rows read all."""
+    T, S = 4096, 64
+    _, rows = oracle.count(BIGBIRD, T, per_row=True)
+    assert (rows[:128] == T).all()
+    n512 = 0
+    for i in range(128, T, 7):
+        qb = i // S
+        blocks = {qb - 1, qb, qb + 1} & set(range(T // S))
+        blocks |= set(oracle.random_blocks(BIGBIRD, T, qb)) | {0, 1}
+        assert rows[i] == S * len(blocks) <= 512
+        n512 += rows[i] == 512
+    assert n512 > 400  # most rows see disjoint blocks
+
+
+def test_random_blocks_are_distinct_in_range_and_seeded():
+    T = 8192
+    nkb = T // 64
+    seen = np.zeros(nkb)
+    for qb in range(nkb):
+        r = oracle.random_blocks(BIGBIRD, T, qb)
+        assert len(r) == 3 and len(set(r)) == 3 and all(0 <= x < nkb for x in r)
+        seen[r] += 1
+    other = BIGBIRD.replace("seed=0", "seed=1")
+    assert any(oracle.random_blocks(other, T, qb) != oracle.random_blocks(BIGBIRD, T, qb)
+               for qb in range(8))
+    # uniform draws: 384 draws over 128 blocks, no block wildly over-used
+    assert seen.max() <= 12
+    # fewer key blocks than R: every block is taken
+    assert sorted(oracle.random_blocks("blocks;block=64;random=5", 200, 0)) == [0, 1, 2, 3]
+
+
+def test_block_size_one_is_the_token_radius():
+    """With block=1 and no random blocks, block distance is token distance:
+    the pinned bidirectional radius rule."""
+    for r in [0, 2, 7]:
+        a, b = f"blocks;block=1;radius={r};global=3", f"bidir;radius={r};global=3"
+        assert oracle.count(a, 50) == oracle.count(b, 50)
+        assert np.array_equal(oracle.dense_mask(a, 50), oracle.dense_mask(b, 50))
+
+
+def test_block_band_count_closed_form():
+    """Without random or global blocks, block qb reads the 2r+1 blocks around
+    it (cut at the ends): E = S * S * sum_qb (min(qb+r, n-1) - max(qb-r, 0) + 1)."""
+    S, n, r = 16, 10, 1
+    expect = S * S * sum(min(q + r, n - 1) - max(q - r, 0) + 1 for q in range(n))
+    assert oracle.count(f"blocks;block={S};radius={r}", S * n) == expect
+
+
+@pytest.mark.parametrize("spec", [BIGBIRD, "blocks;block=16;radius=0;random=2;seed=5;stride=11",
+                                  "blocks;block=8;radius=2;random=1;global=4:9"])
+def test_block_mode_forward_matches_dense_formulation(spec):
+    T = 130
+    q, k, v = _rand(1, 2, T, 16, 31)
+    O, _, _ = oracle.forward_rows(spec, q, k, v)
+    assert np.allclose(O, oracle.dense_forward(spec, q, k, v), rtol=1e-12, atol=1e-12)
+    mask = torch.from_numpy(oracle.dense_mask(spec, T))
+    assert np.allclose(O, _sdpa64(q, k, v, mask=mask), rtol=1e-12, atol=1e-12)
