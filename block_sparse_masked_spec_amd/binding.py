@@ -57,6 +57,7 @@ class sa_mask(ctypes.Structure):
         ("n_global", ctypes.c_int32), ("dilation", ctypes.c_int32),
         ("global_lo", ctypes.c_int64 * SA_MAX_GLOBAL_RANGES),
         ("global_hi", ctypes.c_int64 * SA_MAX_GLOBAL_RANGES),
+        ("block", ctypes.c_int64), ("n_random", ctypes.c_int32), ("seed", ctypes.c_uint32),
     ]
 
 

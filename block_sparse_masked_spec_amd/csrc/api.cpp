@@ -71,6 +71,8 @@ class PlanCache {
         section(hp.colkeys.size() * 4, &dp.off_colkeys);
         section(hp.colbits.size() * 8, &dp.off_colbits);
         section(hp.rowbits.size() * 4, &dp.off_rowbits);
+        section(hp.blk_ptr.size() * 4, &dp.off_blk_ptr);
+        section(hp.blk_iv.size() * 4, &dp.off_blk_iv);
         dp.bytes = align_up(off, 16) + 16;
         std::vector<unsigned char> host(dp.bytes, 0);
         auto put = [&](size_t where, const void* src, size_t bytes) {
@@ -83,6 +85,8 @@ class PlanCache {
         put(dp.off_colkeys, hp.colkeys.data(), hp.colkeys.size() * 4);
         put(dp.off_colbits, hp.colbits.data(), hp.colbits.size() * 8);
         put(dp.off_rowbits, hp.rowbits.data(), hp.rowbits.size() * 4);
+        put(dp.off_blk_ptr, hp.blk_ptr.data(), hp.blk_ptr.size() * 4);
+        put(dp.off_blk_iv, hp.blk_iv.data(), hp.blk_iv.size() * 4);
         if (hipMalloc(&dp.base, dp.bytes) != hipSuccess) {
             (void)hipGetLastError();
             return SA_ERR_NOMEM;
@@ -232,6 +236,9 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     a.colkeys = reinterpret_cast<const int32_t*>(base + dp.off_colkeys);
     a.colbits = reinterpret_cast<const uint64_t*>(base + dp.off_colbits);
     a.rowbits = reinterpret_cast<const uint32_t*>(base + dp.off_rowbits);
+    a.blk = static_cast<int32_t>(m.block);
+    a.blk_ptr = reinterpret_cast<const int32_t*>(base + dp.off_blk_ptr);
+    a.blk_iv = reinterpret_cast<const int32_t*>(base + dp.off_blk_iv);
     const int64_t grid = int64_t(a.BH) * dp.n_qb;
     int lrc = sa::launch_fwd_fast(dtype, d, a, grid, stream);
     if (lrc == SA_ERR_UNSUPPORTED && sub == 1) lrc = sa::launch_fwd(dtype, d, a, grid, stream);

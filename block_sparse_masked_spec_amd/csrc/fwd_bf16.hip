@@ -116,29 +116,11 @@ __device__ __forceinline__ void cursor_advance(Cursor& c, const FwdArgs& a) {
     }
 }
 
-// Bits [0, n) set, n clamped to [0, 64].
-__device__ __forceinline__ uint64_t low_bits(int n) {
-    return n <= 0 ? 0ull : (n >= 64 ? ~0ull : ((1ull << n) - 1ull));
-}
-
-// Allowed keys of query qi among the 64 keys starting at k0, as a bit word:
-// (band OR column bits OR a global query row) AND key < T AND the causal cut.
-// The band is the distance range thinned to the dilation grid; qres = qi mod
-// g and k0res = k0 mod g (both 0 when g = 1).
+// Allowed keys of query qi in the tile at k0 (allowed_word with the tile's
+// column bits read through the scalar cache).
 __device__ __forceinline__ uint64_t rule_word(const FwdArgs& a, int qi, int k0, bool rowg,
-                                              int qres, int k0res) {
-    uint64_t w = rowg ? ~0ull : ldc(a.colbits, k0 >> 6);
-    const long lo = long(qi) - a.band_back - k0;           // first band offset
-    const long hi = long(qi) + long(a.band_fwd) - k0 + 1;  // one past the last
-    if (!rowg && hi > 0 && lo < 64) {
-        const int l0 = lo < 0 ? 0 : int(lo), h0 = hi > 64 ? 64 : int(hi);
-        uint64_t band = low_bits(h0) & ~low_bits(l0);
-        if (a.dil != 1) band &= grid_word(a.dil_pat, a.dil, qres, k0res);
-        w |= band;
-    }
-    w &= low_bits(a.T - k0);
-    if (a.causal) w &= low_bits(qi - k0 + 1);
-    return w;
+                                              int qres, int k0res, int qblk) {
+    return allowed_word(a, qi, k0, rowg, ldc(a.colbits, k0 >> 6), qres, k0res, qblk);
 }
 
 // Tile row (key slot 0..63) that load gi of a tile, lane `lane`, copies, and
@@ -343,6 +325,7 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
     WaveState<D, NG, NW> st;
     bool rowg[NG];
     int qres[NG];  // query index mod the dilation
+    int qblk[NG];  // block mode: the query's block (padding rows use the last row's)
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const int qi = q_base + g * 32 + n;
@@ -358,6 +341,7 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
         st.l_run[g] = 0.f;
         rowg[g] = qi < T && ((a.rowbits[qi >> 5] >> (qi & 31)) & 1u);
         qres[g] = a.dil == 1 ? 0 : qi % a.dil;
+        qblk[g] = a.blk > 0 ? min(qi, T - 1) / a.blk : 0;
     }
 
     const int ga0 = ldc(a.gseg, 4 * qb), ga1 = ldc(a.gseg, 4 * qb + 1);
@@ -375,7 +359,7 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
             allowed[g] = ~0ull;
             if (masked)
                 allowed[g] = c.inplace() ? rule_word(a, q_base + g * 32 + n, c.kb * kBK, rowg[g],
-                                                     qres[g], k0res)
+                                                     qres[g], k0res, qblk[g])
                                          : low_bits(min(kBK, c.g_total - c.gi));
         }
         st.tile(kt, vt, a, lane, masked, allowed);

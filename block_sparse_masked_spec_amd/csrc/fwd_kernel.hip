@@ -176,20 +176,16 @@ struct WaveState {
                                 qf[ks], s[blk]);
         }
         if (MODE == MASK_RULE) {
-            const uint64_t cw = a.colbits[k0 >> 6];
-            const uint64_t gw =
-                a.dil == 1 ? ~0ull : grid_word(a.dil_pat, a.dil, qi % a.dil, k0 % a.dil);
+            // One allowed-key word per lane, then a select per score.
+            const uint64_t aw = allowed_word(
+                a, qi, k0, rowg, a.colbits[k0 >> 6], a.dil == 1 ? 0 : qi % a.dil,
+                a.dil == 1 ? 0 : k0 % a.dil, a.blk > 0 ? min(qi, a.T - 1) / a.blk : 0);
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int ko = blk * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
-                    const int j = k0 + ko;
-                    const bool band = (qi - j <= a.band_back) && (j - qi <= a.band_fwd) &&
-                                      ((gw >> ko) & 1);
-                    const bool ok = j < a.T && (!a.causal || j <= qi) &&
-                                    (band || ((cw >> ko) & 1) || rowg);
-                    if (!ok) s[blk][r] = -INFINITY;
+                    s[blk][r] = ((aw >> ko) & 1) ? s[blk][r] : -INFINITY;
                 }
         } else if (MODE == MASK_SLOTS) {
 #pragma unroll

@@ -18,6 +18,7 @@ std::string canonical_spec(const sa_mask& m);
 // in causal mode, rg on each side in bidir mode (g = dilation); -1 when the
 // band is unlimited.
 inline int64_t band_reach(const sa_mask& m) {
+    if (m.block > 0) return -2;  // block mode: no token band (see band_reach32)
     const int64_t g = m.dilation > 1 ? m.dilation : 1;
     if (m.causal) return m.window == 0 ? -1 : (m.window - 1) * g;
     return m.has_radius ? m.radius * g : -1;
@@ -27,8 +28,14 @@ inline int64_t band_reach(const sa_mask& m) {
 // reach >= T is the same band).
 inline int32_t band_reach32(const sa_mask& m) {
     const int64_t r = band_reach(m);
+    if (r == -2) return -1;  // empty band: i - j <= -1 and j - i <= -1 never hold
     return r < 0 || r > INT32_MAX ? INT32_MAX : static_cast<int32_t>(r);
 }
+
+// Random key blocks of query block qb in block mode ("Rand(qb)" of
+// sparse_attn.h): SplitMix64 from state (seed << 32) | qb, block (x >> 32)
+// mod nkb per output, repeats skipped, at most 64 R draws.
+std::vector<int64_t> random_key_blocks(const sa_mask& m, int64_t nkb, int64_t qb);
 
 // The mask rule of sparse_attn.h for one sequence length, with prefix counts
 // of "column-rule" keys (strided or global) and of global rows so that the
@@ -40,6 +47,12 @@ class MaskRule {
     int64_t T() const { return T_; }
     bool causal() const { return m_.causal != 0; }
     int64_t dilation() const { return g_; }
+    int64_t block() const { return S_; }
+    // Block mode: allowed key-block intervals [kb0, kb1) of query block qb,
+    // sorted and disjoint: ivals()[2t], ivals()[2t+1] for t in
+    // [iv_ptr()[qb], iv_ptr()[qb + 1]).
+    const std::vector<int32_t>& iv_ptr() const { return iv_ptr_; }
+    const std::vector<int32_t>& ivals() const { return ivals_; }
     bool row_global(int64_t i) const { return rowpre_[i + 1] != rowpre_[i]; }
     bool col_key(int64_t j) const { return colpre_[j + 1] != colpre_[j]; }
     int64_t rows_global_in(int64_t a, int64_t b) const { return rowpre_[b] - rowpre_[a]; }
@@ -75,6 +88,8 @@ class MaskRule {
     std::vector<int64_t> colpre_;  // T + 1 entries
     std::vector<int64_t> rowpre_;  // T + 1 entries
     std::vector<int64_t> colres_;  // g > 1: column keys k <= j with k = j (mod g)
+    int64_t S_ = 0;                // block size (block mode) or 0
+    std::vector<int32_t> iv_ptr_, ivals_;
 };
 
 // Execution plan for one (spec, T, tile shape).  All counts per (b, h).
@@ -87,6 +102,8 @@ struct HostPlan {
     std::vector<int32_t> colkeys;   // sorted keys that are strided or global
     std::vector<uint64_t> colbits;  // bit j%64 of word j/64: key j is a colkey
     std::vector<uint32_t> rowbits;  // bit i%32 of word i/32: row i is global
+    std::vector<int32_t> blk_ptr;   // block mode: copies of MaskRule::iv_ptr/ivals
+    std::vector<int32_t> blk_iv;
     int64_t inplace_tiles = 0, masked_tiles = 0, gathered_tiles = 0, gathered_keys = 0;
 };
 
@@ -98,7 +115,7 @@ struct DevicePlan {
     size_t bytes = 0;
     int32_t n_qb = 0;
     size_t off_qb_order = 0, off_run_ptr = 0, off_runs = 0, off_gseg = 0, off_colkeys = 0,
-           off_colbits = 0, off_rowbits = 0;
+           off_colbits = 0, off_rowbits = 0, off_blk_ptr = 0, off_blk_iv = 0;
 };
 
 // Kernel arguments (passed by value).
@@ -114,6 +131,11 @@ struct FwdArgs {
     int32_t band_fwd;
     int32_t dil;       // dilation g >= 1
     uint64_t dil_pat;  // bits 0, g, 2g, ... below 64
+    // Block mode: query block i / blk of query i may read the key blocks in
+    // the intervals blk_iv[2t], blk_iv[2t+1] for t in [blk_ptr[qb], blk_ptr[qb+1]).
+    int32_t blk;  // 0 = token mode
+    const int32_t* blk_ptr;
+    const int32_t* blk_iv;
     // Interleaved subsequences: with sub > 1 each of the BH sequences above is
     // one residue class r of a sequence of T * sub rows (rows r, r + sub, ...),
     // BH counts (b, h, r) triples, and rows sit sub * d elements apart.

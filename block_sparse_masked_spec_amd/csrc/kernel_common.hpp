@@ -2,6 +2,9 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.hpp"
 
 namespace sa {
 
@@ -25,6 +28,49 @@ __device__ __forceinline__ uint64_t grid_word(uint64_t pat, int g, int qres, int
     int start = qres - k0res;
     if (start < 0) start += g;
     return start < 64 ? pat << start : 0ull;
+}
+
+// Block mode: bit x is set iff key k0 + x lies in one of the allowed key-block
+// intervals [iv[2t], iv[2t+1]) (in blocks of size blk) of query block qblk.
+__device__ __forceinline__ uint64_t block_word(int blk, const int32_t* ptr, const int32_t* iv,
+                                               int qblk, int k0) {
+    uint64_t w = 0;
+    for (int t = ptr[qblk]; t < ptr[qblk + 1]; ++t) {
+        const long lo = long(iv[2 * t]) * blk - k0, hi = long(iv[2 * t + 1]) * blk - k0;
+        if (hi > 0 && lo < 64) {
+            const int l0 = lo < 0 ? 0 : int(lo), h0 = hi > 64 ? 64 : int(hi);
+            w |= (h0 >= 64 ? ~0ull : ((1ull << h0) - 1ull)) & ~((1ull << l0) - 1ull);
+        }
+    }
+    return w;
+}
+
+// Bits [0, n) set, n clamped to [0, 64].
+__device__ __forceinline__ uint64_t low_bits(int n) {
+    return n <= 0 ? 0ull : (n >= 64 ? ~0ull : ((1ull << n) - 1ull));
+}
+
+// Allowed keys of query qi among the 64 keys starting at k0, as a bit word:
+// (band OR column keys OR block-mode key blocks OR a global query row) AND
+// key < T AND the causal cut.  colw is the column-key bit word of the tile;
+// the band is the distance range thinned to the dilation grid (qres = qi mod
+// g, k0res = k0 mod g, both 0 when g = 1); qblk is the query's block in
+// block mode, where the token band is empty.
+__device__ __forceinline__ uint64_t allowed_word(const FwdArgs& a, int qi, int k0, bool rowg,
+                                                 uint64_t colw, int qres, int k0res, int qblk) {
+    uint64_t w = rowg ? ~0ull : colw;
+    const long lo = long(qi) - a.band_back - k0;           // first band offset
+    const long hi = long(qi) + long(a.band_fwd) - k0 + 1;  // one past the last
+    if (!rowg && hi > 0 && lo < 64) {
+        const int l0 = lo < 0 ? 0 : int(lo), h0 = hi > 64 ? 64 : int(hi);
+        uint64_t band = low_bits(h0) & ~low_bits(l0);
+        if (a.dil != 1) band &= grid_word(a.dil_pat, a.dil, qres, k0res);
+        w |= band;
+    }
+    if (a.blk > 0 && !rowg) w |= block_word(a.blk, a.blk_ptr, a.blk_iv, qblk, k0);
+    w &= low_bits(a.T - k0);
+    if (a.causal) w &= low_bits(qi - k0 + 1);
+    return w;
 }
 
 }  // namespace sa

@@ -4,7 +4,9 @@
 // section 1 "Intuition" and section 4 "Build it from scratch": a causal or
 // bidirectional base, a local window (causal, counting the query) or radius
 // (bidirectional), strided landmark columns with a phase, and global tokens;
-// plus a dilation of the local window (section 6, the dilated-mask exercise).
+// plus a dilation of the local window (section 6, the dilated-mask exercise),
+// and a block mode for BigBird ("Sparse and sliding-window attention",
+// section "Block-sparse attention: BigBird").
 // The grammar is documented in include/sparse_attn.h.
 #include "internal.hpp"
 
@@ -81,16 +83,18 @@ int parse_mask_spec(const char* text, sa_mask* out) {
     if (!c.word(&mode)) return SA_ERR_SPEC;
     sa_mask m;
     std::memset(&m, 0, sizeof(m));
+    const bool blocks = mode == "blocks";
     if (mode == "causal")
         m.causal = 1;
-    else if (mode == "bidir")
+    else if (mode == "bidir" || blocks)
         m.causal = 0;
     else
         return SA_ERR_SPEC;
 
     m.dilation = 1;
     bool seen_window = false, seen_radius = false, seen_stride = false, seen_phase = false,
-         seen_global = false, seen_dilation = false;
+         seen_global = false, seen_dilation = false, seen_block = false, seen_random = false,
+         seen_seed = false;
     std::vector<std::pair<int64_t, int64_t>> ranges;
     while (c.eat(';')) {
         std::string key;
@@ -102,7 +106,22 @@ int parse_mask_spec(const char* text, sa_mask* out) {
         }
         int64_t v = 0;
         if (!c.number(&v)) return SA_ERR_SPEC;
-        if (key == "window") {
+        const bool block_only = key == "block" || key == "random" || key == "seed";
+        const bool token_only = key == "window" || key == "dilation";
+        if ((block_only && !blocks) || (token_only && blocks)) return SA_ERR_SPEC;
+        if (key == "block") {
+            if (seen_block || v < 1) return SA_ERR_SPEC;
+            seen_block = true;
+            m.block = v;
+        } else if (key == "random") {
+            if (seen_random || v > 4096) return SA_ERR_SPEC;
+            seen_random = true;
+            m.n_random = static_cast<int32_t>(v);
+        } else if (key == "seed") {
+            if (seen_seed) return SA_ERR_SPEC;
+            seen_seed = true;
+            m.seed = static_cast<uint32_t>(v);
+        } else if (key == "window") {
             if (seen_window || !m.causal) return SA_ERR_SPEC;
             seen_window = true;
             m.window = v;
@@ -128,6 +147,10 @@ int parse_mask_spec(const char* text, sa_mask* out) {
         }
     }
     if (!c.done()) return SA_ERR_SPEC;
+    if (blocks) {
+        if (!seen_block) return SA_ERR_SPEC;
+        m.has_radius = 1;  // radius counts blocks; absent = 0 (the query's own block)
+    }
     if (seen_phase && m.stride == 0) return SA_ERR_SPEC;
     if (m.stride > 0 && m.phase >= m.stride) return SA_ERR_SPEC;
 
@@ -151,7 +174,10 @@ int parse_mask_spec(const char* text, sa_mask* out) {
 }
 
 std::string canonical_spec(const sa_mask& m) {
-    std::string s = m.causal ? "causal" : "bidir";
+    std::string s = m.causal ? "causal" : (m.block > 0 ? "blocks" : "bidir");
+    if (m.block > 0)
+        s += ";block=" + std::to_string(m.block) + ";random=" + std::to_string(m.n_random) +
+             ";seed=" + std::to_string(m.seed);
     if (m.causal) s += ";window=" + std::to_string(m.window);
     if (!m.causal && m.has_radius) s += ";radius=" + std::to_string(m.radius);
     if (m.dilation != 1) s += ";dilation=" + std::to_string(m.dilation);

@@ -16,8 +16,53 @@
 
 namespace sa {
 
+std::vector<int64_t> random_key_blocks(const sa_mask& m, int64_t nkb, int64_t qb) {
+    std::vector<int64_t> out;
+    if (m.n_random <= 0) return out;
+    if (nkb <= m.n_random) {
+        for (int64_t kb = 0; kb < nkb; ++kb) out.push_back(kb);
+        return out;
+    }
+    // SplitMix64 (Steele, Lea and Flood, OOPSLA 2014): add the golden gamma,
+    // then two xor-shift-multiply rounds and a final xor-shift.
+    uint64_t state = (uint64_t(m.seed) << 32) | uint64_t(qb);
+    for (int64_t draw = 0; draw < 64 * int64_t(m.n_random) && int64_t(out.size()) < m.n_random;
+         ++draw) {
+        state += 0x9E3779B97F4A7C15ull;
+        uint64_t z = state;
+        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+        z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+        z ^= z >> 31;
+        const int64_t kb = int64_t((z >> 32) % uint64_t(nkb));
+        if (std::find(out.begin(), out.end(), kb) == out.end()) out.push_back(kb);
+    }
+    return out;
+}
+
 MaskRule::MaskRule(const sa_mask& m, int64_t T)
     : m_(m), T_(T), g_(m.dilation > 1 ? m.dilation : 1), colpre_(T + 1, 0), rowpre_(T + 1, 0) {
+    if (m.block > 0) {  // block mode: merged intervals of allowed key blocks per query block
+        S_ = m.block;
+        const int64_t nb = (T + S_ - 1) / S_;
+        iv_ptr_.push_back(0);
+        for (int64_t qb = 0; qb < nb; ++qb) {
+            std::vector<std::pair<int64_t, int64_t>> iv;
+            iv.emplace_back(std::max<int64_t>(0, qb - m.radius), std::min<int64_t>(nb, qb + m.radius + 1));
+            for (int64_t kb : random_key_blocks(m, nb, qb)) iv.emplace_back(kb, kb + 1);
+            std::sort(iv.begin(), iv.end());
+            int64_t n0 = static_cast<int64_t>(ivals_.size());
+            for (const auto& x : iv) {
+                const int64_t n = static_cast<int64_t>(ivals_.size());
+                if (n > n0 && x.first <= ivals_[n - 1])
+                    ivals_[n - 1] = static_cast<int32_t>(std::max<int64_t>(ivals_[n - 1], x.second));
+                else {
+                    ivals_.push_back(static_cast<int32_t>(x.first));
+                    ivals_.push_back(static_cast<int32_t>(x.second));
+                }
+            }
+            iv_ptr_.push_back(static_cast<int32_t>(ivals_.size() / 2));
+        }
+    }
     std::vector<uint8_t> glob(T, 0);
     for (int k = 0; k < m.n_global; ++k)
         for (int64_t x = m.global_lo[k]; x < m.global_hi[k] && x < T; ++x) glob[x] = 1;
@@ -34,11 +79,13 @@ MaskRule::MaskRule(const sa_mask& m, int64_t T)
 }
 
 int64_t MaskRule::band_lo(int64_t i) const {
+    if (S_ > 0) return 0;  // block mode: the plan scans every key tile
     const int64_t r = band_reach(m_);
     return r < 0 ? 0 : std::max<int64_t>(0, i - r);
 }
 
 int64_t MaskRule::band_hi(int64_t i) const {
+    if (S_ > 0) return T_ - 1;
     if (m_.causal) return i;
     const int64_t r = band_reach(m_);
     return r < 0 ? T_ - 1 : std::min<int64_t>(T_ - 1, i + r);
@@ -70,6 +117,16 @@ int64_t MaskRule::allowed_in(int64_t i, int64_t a, int64_t b) const {
     b = std::min<int64_t>(b, key_limit(i) + 1);  // causal cut
     if (a >= b) return 0;
     if (row_global(i)) return b - a;
+    if (S_ > 0) {  // block mode: keys of the allowed key blocks, plus column keys elsewhere
+        const int64_t qb = i / S_;
+        int64_t n = col_keys_in(a, b);
+        for (int32_t t = iv_ptr_[qb]; t < iv_ptr_[qb + 1]; ++t) {
+            const int64_t lo = std::max(a, int64_t(ivals_[2 * t]) * S_);
+            const int64_t hi = std::min(b, int64_t(ivals_[2 * t + 1]) * S_);
+            if (lo < hi) n += (hi - lo) - col_keys_in(lo, hi);
+        }
+        return n;
+    }
     int64_t lo = std::max(a, band_lo(i)), hi = std::min(b, band_hi(i) + 1);
     if (lo >= hi) return col_keys_in(a, b);
     return on_grid(i, lo, hi) + col_keys_in(a, b) - col_keys_on_grid(i, lo, hi);
@@ -79,7 +136,16 @@ int MaskRule::classify(int64_t q0, int64_t q1, int64_t k0, int64_t k1) const {
     q1 = std::min(q1, T_);
     k1 = std::min(k1, T_);
     if (q0 >= q1 || k0 >= k1) return SA_TILE_EMPTY;
-    if (rows_global_in(q0, q1) == 0) {
+    if (S_ > 0 && rows_global_in(q0, q1) == 0 && col_keys_in(k0, k1) == 0) {
+        // Block mode: empty unless some query block of the rows allows a key
+        // block that meets the tile.
+        bool meets = false;
+        for (int64_t qb = q0 / S_; qb <= (q1 - 1) / S_ && !meets; ++qb)
+            for (int32_t t = iv_ptr_[qb]; t < iv_ptr_[qb + 1]; ++t)
+                meets |= int64_t(ivals_[2 * t]) * S_ < k1 && k0 < int64_t(ivals_[2 * t + 1]) * S_;
+        if (!meets) return SA_TILE_EMPTY;
+    }
+    if (S_ == 0 && rows_global_in(q0, q1) == 0) {
         // Band ends are monotone in i: the first row has the lowest upper
         // end, the last row the highest lower end.
         if (g_ == 1 && k0 >= band_lo(q1 - 1) && k1 - 1 <= band_hi(q0)) return SA_TILE_FULL;
@@ -109,6 +175,8 @@ HostPlan build_plan(const MaskRule& rule, int32_t bq, int32_t bk) {
         }
         if (rule.row_global(j)) p.rowbits[j >> 5] |= uint32_t(1) << (j & 31);
     }
+    p.blk_ptr = rule.iv_ptr();
+    p.blk_iv = rule.ivals();
     std::vector<int64_t> work(p.n_qb, 0);
     p.run_ptr.push_back(0);
     p.gseg.resize(4 * static_cast<size_t>(p.n_qb));

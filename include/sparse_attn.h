@@ -29,15 +29,31 @@
  *   Gl = i in G or j in G (global tokens read and are read by everyone;
  *        in causal mode C still applies, "Attention variants" section 4).
  *
+ * Block mode (BigBird: "Sparse and sliding-window attention", getnybble.com,
+ * section "Block-sparse attention: BigBird", a window of 3 blocks, R random
+ * blocks, G global blocks).  With block size S, qb = i / S and kb = j / S:
+ *   allowed(i,j) = |qb - kb| <= radius or kb in Rand(qb) or St or Gl,
+ * bidirectional.  Rand(qb) holds R distinct key blocks drawn uniformly from
+ * all ceil(T/S) blocks (local and global ones included): SplitMix64 (Steele,
+ * Lea and Flood, OOPSLA 2014) started from state (seed << 32) | qb, each
+ * output x naming block (x >> 32) mod ceil(T/S); repeats are skipped, at most
+ * 64 R draws are made, and with ceil(T/S) <= R every block is taken.
+ *
  * Mask-spec grammar (whitespace ignored; integers are decimal, >= 0,
  * < 2^31; a key may appear once):
  *   spec   := ('causal' | 'bidir') (';' clause)*
+ *           | 'blocks' ';' 'block=' INT (';' bclause)*
  *   clause := 'window=' INT        causal only; 0 = unlimited (full causal)
  *           | 'radius=' INT        bidir only; absent = unlimited
  *           | 'dilation=' INT      >= 1; local keys sit this far apart
  *           | 'stride=' INT        0 = no strided columns
  *           | 'phase='  INT        needs stride > 0; 0 <= phase < stride
  *           | 'global=' R (',' R)* R := INT | INT ':' INT  (half-open, a < b)
+ *   bclause := 'radius=' INT       in blocks; default 0 (own block)
+ *           | 'random=' INT        random key blocks per query block, <= 4096
+ *           | 'seed=' INT          default 0
+ *           | 'stride=' INT | 'phase=' INT | 'global=' ...   as above
+ *   ('block=' may stand anywhere among the block-mode clauses; S >= 1.)
  *
  * Tensor layout.  Q, K, V, O are dense row-major [B][H][T][d] device arrays
  * of one element type (bf16 for sparse_attn_fwd, fp32 for
@@ -105,6 +121,10 @@ typedef struct sa_mask {
     int32_t dilation;   /* >= 1 */
     int64_t global_lo[SA_MAX_GLOBAL_RANGES];
     int64_t global_hi[SA_MAX_GLOBAL_RANGES];
+    int64_t block;      /* > 0: block mode with block size `block`; radius
+                           then counts blocks */
+    int32_t n_random;   /* block mode: random key blocks per query block */
+    uint32_t seed;      /* block mode: random stream seed */
 } sa_mask;
 
 /* Summary of the plan the kernel runs for (spec, T, d, dtype).  Counts are

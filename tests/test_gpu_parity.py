@@ -98,6 +98,10 @@ SMALL_SPECS = [
     "causal;window=4;dilation=70",
     "bidir;radius=7;dilation=3",
     "causal;window=0;dilation=4",
+    "blocks;block=64;radius=1;random=3;seed=0;global=0:8",
+    "blocks;block=16;random=2;seed=3",
+    "blocks;block=100;radius=1;random=1;seed=1",
+    "blocks;block=8;radius=2;random=4;stride=37;global=150",
 ]
 
 
@@ -197,6 +201,15 @@ def test_cfg_dilated_16k(gpu):
     apart (the W=512, dilation 2 example of the dilated sliding window)."""
     sampled_check(gpu, "causal;window=512;dilation=2", 1, 16, 16384, 128, seed=0,
                   extra=(1021, 1022, 1023, 1024, 1025, 4097))
+
+
+def test_cfg_bigbird_4k(gpu):
+    """BigBird block pattern (block 64, 3-block window, 3 random blocks, 2
+    global blocks), B=8, H=12, T=4096, d=64: sampled rows at the bench
+    shape, and every row of one head-pair batch."""
+    spec = "blocks;block=64;radius=1;random=3;seed=0;global=0:128"
+    sampled_check(gpu, spec, 8, 12, 4096, 64, seed=0, extra=(0, 127, 128, 191, 192, 4095))
+    full_check(gpu, spec, 1, 2, 4096, 64, "bf16", seed=1)
 
 
 def test_cfg_gemma_interleave(gpu):

@@ -33,10 +33,32 @@ CONFIG_SPECS = [
     ("causal;window=512;dilation=2", 4096),
     ("bidir;radius=64;dilation=4;stride=128;phase=5;global=0:8", 2048),
     ("causal;window=0;dilation=3;global=100:104", 1000),
+    ("blocks;block=64;radius=1;random=3;seed=0;global=0:128", 4096),
+    ("blocks;block=32;radius=2;random=5;seed=7;stride=100", 2000),
 ]
 
 
+def random_block_spec(rng: random.Random, T: int) -> str:
+    parts = ["blocks", f"block={rng.choice([1, 3, 8, 16, 64, 100])}"]
+    if rng.random() < 0.8:
+        parts.append(f"radius={rng.choice([0, 1, 2, 5])}")
+    if rng.random() < 0.8:
+        parts.append(f"random={rng.choice([0, 1, 3, 7])}")
+        if rng.random() < 0.7:
+            parts.append(f"seed={rng.randrange(1000)}")
+    if rng.random() < 0.3:
+        parts.append(f"stride={rng.choice([5, 16])}")
+    if rng.random() < 0.4:
+        a = rng.randrange(T)
+        parts.append(f"global={a}:{min(T, a + rng.randint(1, 9))}")
+    clauses = parts[1:]
+    rng.shuffle(clauses)
+    return ";".join(parts[:1] + clauses)
+
+
 def random_spec(rng: random.Random, T: int) -> str:
+    if rng.random() < 0.2:
+        return random_block_spec(rng, T)
     causal = rng.random() < 0.6
     parts = ["causal" if causal else "bidir"]
     if causal:
@@ -104,6 +126,9 @@ def test_plan_info_struct_size_matches_header():
     "bidir;global=5:5", "bidir;global=a", "causal;window", "causal;stride=4;phase=x",
     "causal;window=99999999999", "causal;;window=2", "causal;window=2;", "causal window=2",
     "causal;dilation=0", "causal;window=4;dilation=2;dilation=3", "bidir;dilation=",
+    "blocks", "blocks;radius=1", "blocks;block=0", "blocks;block=64;window=3",
+    "blocks;block=64;dilation=2", "bidir;block=64", "causal;random=3", "bidir;seed=1",
+    "blocks;block=64;random=4097", "blocks;block=64;block=32",
 ])
 def test_parser_rejects(bad):
     with pytest.raises(sa.SparseAttnError) as e:
@@ -122,6 +147,8 @@ def test_parser_fields_and_normalisation():
     assert (c.causal, c.window, c.stride, c.phase, c.dilation) == (1, 0, 4, 3, 1)
     g = sa.sparse_attn_parse("causal;dilation=3;window=8")
     assert (g.window, g.dilation) == (8, 3)
+    b = sa.sparse_attn_parse("blocks;random=3;block=64;seed=9;global=0:128")
+    assert (b.causal, b.block, b.n_random, b.seed, b.radius) == (0, 64, 3, 9, 0)
 
 
 def test_parser_null_arguments():
