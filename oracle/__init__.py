@@ -15,6 +15,10 @@ What it computes (fp64, no rounding of the result):
   every key, scores q.k/sqrt(d), max, exp-sum and the renormalised weighted
   sum of values ("Sparse attention", glossary.selfmadequant.com, section
   "Choose the available reads").
+* ``backward`` -- dQ, dK, dV for an upstream gradient dO: the chain rule
+  through the renormalised softmax, row by row (pinned by finite differences
+  of ``forward_rows``, by autograd through a dense masked softmax, and by the
+  identities sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i).
 * ``dense_forward`` -- a second, independent formulation for tiny inputs: a
   materialised boolean mask, full score matrix, -inf fill, softmax, matmul
   (the naive recipe of "Sparse and sliding-window attention", getnybble.com,
@@ -228,6 +232,11 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
             ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_forward_rows.restype = ctypes.c_int
+        lib.oracle_backward.argtypes = [
+            P(_CMask), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p]
+        lib.oracle_backward.restype = ctypes.c_int
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
         _lib = lib
@@ -343,6 +352,25 @@ def forward_rows(spec, Q, K, V, rows=None):
     if rows is None:
         return O.reshape(B, H, T, d), lse.reshape(B, H, T), nset.reshape(B, H, T)
     return O, lse, nset
+
+
+def backward(spec, Q, K, V, dO):
+    """Gradients (dQ, dK, dV) of the forward for upstream gradient dO, fp64,
+    each [B, H, T, d].  The chain rule through the softmax over each S_i,
+    written out in sa_oracle.c."""
+    m = _as_mask(spec)
+    q, k, v, g = (_to_f32(x) for x in (Q, K, V, dO))
+    B, H, T, d = q.shape
+    dq = np.zeros((B, H, T, d), dtype=np.float64)
+    dk = np.zeros_like(dq)
+    dv = np.zeros_like(dq)
+    c, keep = _cmask(m)
+    rc = _load().oracle_backward(ctypes.byref(c), q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                 g.ctypes.data, B * H, T, d, dq.ctypes.data, dk.ctypes.data,
+                                 dv.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_backward failed (no memory)")
+    return dq, dk, dv
 
 
 def threads() -> int:

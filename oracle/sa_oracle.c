@@ -267,6 +267,87 @@ int oracle_forward_rows(const oracle_mask* m, const float* Q, const float* K,
     return failed ? -1 : 0;
 }
 
+/*
+ * Backward pass of the same attention (the pages define only the forward;
+ * this is the gradient of its definition, "Choose the available reads",
+ * by the chain rule through the softmax over S_i).  With s_ij = q_i.k_j /
+ * sqrt(d) for j in S_i, p_ij = exp(s_ij - lse_i) and an upstream gradient
+ * dO (the gradient of the loss with respect to O):
+ *   dV_j  = sum_i p_ij dO_i
+ *   dp_ij = dO_i . v_j
+ *   D_i   = sum_j p_ij dp_ij            (= dO_i . o_i)
+ *   ds_ij = p_ij (dp_ij - D_i)
+ *   dQ_i  = sum_j ds_ij k_j / sqrt(d)
+ *   dK_j  = sum_i ds_ij q_i / sqrt(d)
+ * Tensors [BH][T][d] fp32 in, fp64 out (dQ, dK, dV written in full).
+ * Returns 0, or -1 if memory runs out.
+ */
+int oracle_backward(const oracle_mask* m, const float* Q, const float* K, const float* V,
+                    const float* dO, int64_t BH, int64_t T, int64_t d, double* dQ, double* dK,
+                    double* dV) {
+    int failed = 0;
+    const double rscale = sqrt(1.0 / (double)d);
+    for (int64_t x = 0; x < BH * T * d; ++x) dQ[x] = dK[x] = dV[x] = 0.0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        int64_t* set = (int64_t*)malloc(sizeof(int64_t) * (size_t)(T > 0 ? T : 1));
+        double* p = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+        double* dp = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+        if (!set || !p || !dp) {
+            failed = 1;
+        } else {
+            for (int64_t i = 0; i < T; ++i) {
+                const float* q = Q + (bh * T + i) * d;
+                const float* g = dO + (bh * T + i) * d;
+                const int64_t n = oracle_row_set(m, T, i, set);
+                if (n == 0) continue;
+                /* softmax weights over S_i */
+                double mx = -INFINITY;
+                for (int64_t t = 0; t < n; ++t) {
+                    const float* kr = K + d * (bh * T + set[t]);
+                    double qk = 0.0;
+                    for (int64_t c = 0; c < d; ++c) qk += (double)q[c] * (double)kr[c];
+                    p[t] = qk * rscale;
+                    if (p[t] > mx) mx = p[t];
+                }
+                double l = 0.0;
+                for (int64_t t = 0; t < n; ++t) {
+                    p[t] = exp(p[t] - mx);
+                    l += p[t];
+                }
+                for (int64_t t = 0; t < n; ++t) p[t] /= l;
+                /* dp and D */
+                double D = 0.0;
+                for (int64_t t = 0; t < n; ++t) {
+                    const float* vr = V + d * (bh * T + set[t]);
+                    double gv = 0.0;
+                    for (int64_t c = 0; c < d; ++c) gv += (double)g[c] * (double)vr[c];
+                    dp[t] = gv;
+                    D += p[t] * gv;
+                }
+                /* accumulate the three gradients */
+                double* dq = dQ + (bh * T + i) * d;
+                for (int64_t t = 0; t < n; ++t) {
+                    const int64_t j = set[t];
+                    const double ds = p[t] * (dp[t] - D);
+                    const float* kr = K + d * (bh * T + j);
+                    double* dk = dK + d * (bh * T + j);
+                    double* dv = dV + d * (bh * T + j);
+                    for (int64_t c = 0; c < d; ++c) {
+                        dq[c] += ds * (double)kr[c] * rscale;
+                        dk[c] += ds * (double)q[c] * rscale;
+                        dv[c] += p[t] * (double)g[c];
+                    }
+                }
+            }
+        }
+        free(set);
+        free(p);
+        free(dp);
+    }
+    return failed ? -1 : 0;
+}
+
 int oracle_threads(void) {
     int n = 1;
 #pragma omp parallel

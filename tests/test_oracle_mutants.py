@@ -54,6 +54,11 @@ MUTANTS = [
      "const int64_t qb = i / m->block, kb = i / m->block;"),
     ("random_repeats_kept", "if (!seen) out[n++] = kb;", "out[n++] = kb;"),
     ("splitmix_gamma", "0x9E3779B97F4A7C15ull", "0x9E3779B97F4A7C13ull"),
+    ("bwd_delta_dropped", "const double ds = p[t] * (dp[t] - D);", "const double ds = p[t] * dp[t];"),
+    ("bwd_dk_uses_k", "dk[c] += ds * (double)q[c] * rscale;", "dk[c] += ds * (double)kr[c] * rscale;"),
+    ("bwd_dq_unscaled", "dq[c] += ds * (double)kr[c] * rscale;", "dq[c] += ds * (double)kr[c];"),
+    ("bwd_dv_unnormalised", "for (int64_t t = 0; t < n; ++t) p[t] /= l;", ""),
+    ("bwd_dp_uses_k", "const float* vr = V + d * (bh * T + set[t]);", "const float* vr = K + d * (bh * T + set[t]);"),
     ("block_globals_dropped", "return local || rnd || strided_col(m, j) || global_pair(m, i, j);",
      "return local || rnd || strided_col(m, j);"),
 ]
@@ -113,6 +118,18 @@ def _pins_pass() -> bool:
             return False
         if oracle.count("blocks;block=1;radius=2", 40) != oracle.count("bidir;radius=2", 40):
             return False
+        # backward: autograd through a dense masked softmax, and finite differences
+        g = inputs.qkv(1, 2, 33, 16, "f32", 3)[0]
+        for bspec in ["causal;window=5;stride=4;global=2", "causal;window=1"]:
+            dq, dk, dv = oracle.backward(bspec, q, k, v, g)
+            mask = torch.from_numpy(oracle.dense_mask(bspec, 33))
+            Qg, Kg, Vg = (x.double().requires_grad_() for x in (q, k, v))
+            sc = torch.matmul(Qg, Kg.transpose(-1, -2)) / 4.0
+            Og = torch.matmul(torch.softmax(sc.masked_fill(~mask, float("-inf")), -1), Vg)
+            Og.backward(g.double())
+            for got, ref in ((dq, Qg.grad), (dk, Kg.grad), (dv, Vg.grad)):
+                if not np.allclose(got, ref.numpy(), rtol=1e-9, atol=1e-11):
+                    return False
         O1, _, _ = oracle.forward_rows("causal;window=1", q, k, v)
         if not np.array_equal(O1, v.double().numpy()):
             return False
