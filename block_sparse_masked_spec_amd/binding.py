@@ -39,7 +39,8 @@ EXPORTED = [
     "sparse_attn_fwd", "sparse_attn_fwd_f32", "sparse_attn_parse", "sparse_attn_count",
     "sparse_attn_tile_map", "sparse_attn_tile_shape", "sparse_attn_plan_info",
     "sparse_attn_strerror", "sparse_attn_release_cache", "sparse_attn_decode",
-    "sparse_attn_decode_cache_rows",
+    "sparse_attn_decode_cache_rows", "sparse_attn_fwd_lse", "sparse_attn_fwd_lse_f32",
+    "sparse_attn_bwd", "sparse_attn_bwd_f32",
 ]
 
 
@@ -102,6 +103,16 @@ def load():
     lib.sparse_attn_plan_info.restype = i32
     lib.sparse_attn_strerror.argtypes = [i32]
     lib.sparse_attn_strerror.restype = cs
+    lse_args = [vp, vp, vp, vp, vp, i32, i32, i32, i32, cs, vp]
+    lib.sparse_attn_fwd_lse.argtypes = lse_args
+    lib.sparse_attn_fwd_lse.restype = i32
+    lib.sparse_attn_fwd_lse_f32.argtypes = lse_args
+    lib.sparse_attn_fwd_lse_f32.restype = i32
+    bwd_args = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, cs, vp]
+    lib.sparse_attn_bwd.argtypes = bwd_args
+    lib.sparse_attn_bwd.restype = i32
+    lib.sparse_attn_bwd_f32.argtypes = bwd_args
+    lib.sparse_attn_bwd_f32.restype = i32
     lib.sparse_attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, cs, vp]
     lib.sparse_attn_decode.restype = i32
     lib.sparse_attn_decode_cache_rows.argtypes = [cs, i32, ctypes.POINTER(i64)]
@@ -195,6 +206,34 @@ def sparse_attn_plan_info(mask_spec, T, d, dtype=SA_DTYPE_BF16) -> dict:
     _check(load().sparse_attn_plan_info(_spec(mask_spec), T, d, dtype, ctypes.byref(info)),
            "sparse_attn_plan_info")
     return {name: getattr(info, name) for name, _ in sa_plan_info._fields_}
+
+
+def sparse_attn_fwd_lse(Q, K, V, O, LSE, B, H, T, d, mask_spec, stream=None):
+    """bf16 forward that also writes the fp32 log-sum-exp [B, H, T]."""
+    return _check(load().sparse_attn_fwd_lse(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), B, H,
+                                             T, d, _spec(mask_spec), _stream_handle(stream)),
+                  "sparse_attn_fwd_lse")
+
+
+def sparse_attn_fwd_lse_f32(Q, K, V, O, LSE, B, H, T, d, mask_spec, stream=None):
+    return _check(load().sparse_attn_fwd_lse_f32(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), B,
+                                                 H, T, d, _spec(mask_spec), _stream_handle(stream)),
+                  "sparse_attn_fwd_lse_f32")
+
+
+def sparse_attn_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, T, d, mask_spec, stream=None):
+    """bf16 backward: writes dQ, dK, dV."""
+    return _check(load().sparse_attn_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE),
+                                         _ptr(dQ), _ptr(dK), _ptr(dV), B, H, T, d, _spec(mask_spec),
+                                         _stream_handle(stream)),
+                  "sparse_attn_bwd")
+
+
+def sparse_attn_bwd_f32(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, T, d, mask_spec, stream=None):
+    return _check(load().sparse_attn_bwd_f32(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO),
+                                             _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV), B, H, T, d,
+                                             _spec(mask_spec), _stream_handle(stream)),
+                  "sparse_attn_bwd_f32")
 
 
 def sparse_attn_decode(Q, K_cache, V_cache, O, pos, B, H, Hkv, n_new, C, d, mask_spec,

@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["mask_spec.cpp", "plan.cpp", "api.cpp"]
-DEVICE_SOURCES = ["fwd_kernel.hip", "fwd_bf16.hip", "decode.hip"]
+DEVICE_SOURCES = ["fwd_kernel.hip", "fwd_bf16.hip", "decode.hip", "bwd_kernel.hip"]
 
 COMMON = ["-O3", "-std=c++20", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function"]
 # Device code: no packed fp32 ops (v_pk_*_f32) anywhere.

@@ -100,6 +100,51 @@ class PlanCache {
         return SA_OK;
     }
 
+    // The backward plan (key blocks -> query tiles) for (spec, T).
+    int get_bwd(const sa_mask& m, int T, sa::BwdDevicePlan* out) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return SA_ERR_HIP;
+        std::string key = sa::canonical_spec(m) + "|T=" + std::to_string(T) + "|bwd|dev=" +
+                          std::to_string(dev);
+        std::lock_guard<std::mutex> lock(mu_);
+        auto it = bwd_.find(key);
+        if (it != bwd_.end()) {
+            *out = it->second.plan;
+            return SA_OK;
+        }
+        sa::BwdHostPlan hp = sa::build_bwd_plan(MaskRule(m, T));
+        sa::BwdDevicePlan dp;
+        dp.n_kb = hp.n_kb;
+        size_t off = 0;
+        auto section = [&](size_t bytes, size_t* where) {
+            off = align_up(off, 16);
+            *where = off;
+            off += bytes;
+        };
+        section(hp.kb_order.size() * 4, &dp.off_order);
+        section(hp.kb_ptr.size() * 4, &dp.off_ptr);
+        section(hp.kb_runs.size() * 4, &dp.off_runs);
+        dp.bytes = align_up(off, 16) + 16;
+        std::vector<unsigned char> host(dp.bytes, 0);
+        auto put = [&](size_t where, const void* src, size_t bytes) {
+            if (bytes) std::memcpy(host.data() + where, src, bytes);
+        };
+        put(dp.off_order, hp.kb_order.data(), hp.kb_order.size() * 4);
+        put(dp.off_ptr, hp.kb_ptr.data(), hp.kb_ptr.size() * 4);
+        put(dp.off_runs, hp.kb_runs.data(), hp.kb_runs.size() * 4);
+        if (hipMalloc(&dp.base, dp.bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return SA_ERR_NOMEM;
+        }
+        if (hipMemcpy(dp.base, host.data(), dp.bytes, hipMemcpyHostToDevice) != hipSuccess) {
+            (void)hipFree(dp.base);
+            return SA_ERR_HIP;
+        }
+        bwd_.emplace(key, BwdEntry{dp, dev});
+        *out = dp;
+        return SA_OK;
+    }
+
     void release() {
         std::lock_guard<std::mutex> lock(mu_);
         int cur = 0;
@@ -107,8 +152,12 @@ class PlanCache {
         for (auto& kv : plans_) {
             if (hipSetDevice(kv.second.device) == hipSuccess) (void)hipFree(kv.second.plan.base);
         }
+        for (auto& kv : bwd_) {
+            if (hipSetDevice(kv.second.device) == hipSuccess) (void)hipFree(kv.second.plan.base);
+        }
         if (have_cur) (void)hipSetDevice(cur);
         plans_.clear();
+        bwd_.clear();
     }
 
   private:
@@ -116,8 +165,13 @@ class PlanCache {
         DevicePlan plan;
         int device;
     };
+    struct BwdEntry {
+        sa::BwdDevicePlan plan;
+        int device;
+    };
     std::mutex mu_;
     std::unordered_map<std::string, Entry> plans_;
+    std::unordered_map<std::string, BwdEntry> bwd_;
 };
 
 PlanCache& cache() {
@@ -188,7 +242,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int B, int H, int T,
-            int d, const char* spec, void* stream) {
+            int d, const char* spec, void* stream, float* lse = nullptr) {
     if (!Q || !K || !V || !O || !spec) return SA_ERR_NULL;
     if (B < 1 || H < 1 || T < 1 || T > SA_MAX_T) return SA_ERR_SHAPE;
     if (!supported_d(d)) return SA_ERR_UNSUPPORTED;
@@ -201,6 +255,12 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     const size_t bytes = size_t(BH) * size_t(T) * size_t(d) * esz;
     if (overlaps(O, bytes, Q, bytes) || overlaps(O, bytes, K, bytes) || overlaps(O, bytes, V, bytes))
         return SA_ERR_ALIAS;
+    if (lse) {
+        const size_t lbytes = size_t(BH) * size_t(T) * sizeof(float);
+        if (reinterpret_cast<uintptr_t>(lse) % 4) return SA_ERR_ALIGN;
+        for (const void* p : {Q, K, V, static_cast<const void*>(O)})
+            if (overlaps(lse, lbytes, p, bytes)) return SA_ERR_ALIAS;
+    }
     sa_mask m;
     int rc = parse_for(spec, T, &m);
     if (rc != SA_OK) return rc;
@@ -239,10 +299,94 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     a.blk = static_cast<int32_t>(m.block);
     a.blk_ptr = reinterpret_cast<const int32_t*>(base + dp.off_blk_ptr);
     a.blk_iv = reinterpret_cast<const int32_t*>(base + dp.off_blk_iv);
+    a.lse = lse;
     const int64_t grid = int64_t(a.BH) * dp.n_qb;
     int lrc = sa::launch_fwd_fast(dtype, d, a, grid, stream);
     if (lrc == SA_ERR_UNSUPPORTED && sub == 1) lrc = sa::launch_fwd(dtype, d, a, grid, stream);
     return lrc;
+}
+
+// Forward arguments for (spec, T, d): parse, plan lookup and the rule fields.
+// Used by the backward, which runs on the token-level plan (no residue split).
+int backward(int dtype, const void* Q, const void* K, const void* V, const void* O, const void* dO,
+             const float* lse, void* dQ, void* dK, void* dV, int B, int H, int T, int d,
+             const char* spec, void* stream) {
+    if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV || !spec) return SA_ERR_NULL;
+    if (B < 1 || H < 1 || T < 1 || T > SA_MAX_T) return SA_ERR_SHAPE;
+    if (!supported_d(d)) return SA_ERR_UNSUPPORTED;
+    const int64_t BH = int64_t(B) * H;
+    const int64_t n_qb = (int64_t(T) + sa::kBQ - 1) / sa::kBQ;
+    const int64_t n_kb = (int64_t(T) + sa::kBKB - 1) / sa::kBKB;
+    if (BH > INT32_MAX || BH * n_qb > INT32_MAX || BH * n_kb > INT32_MAX) return SA_ERR_SHAPE;
+    for (const void* p : {Q, K, V, O, dO, static_cast<const void*>(dQ), static_cast<const void*>(dK),
+                          static_cast<const void*>(dV)})
+        if (reinterpret_cast<uintptr_t>(p) % 16) return SA_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(lse) % 4) return SA_ERR_ALIGN;
+    const size_t esz = dtype == SA_DTYPE_BF16 ? 2 : 4;
+    const size_t bytes = size_t(BH) * size_t(T) * size_t(d) * esz;
+    const size_t lbytes = size_t(BH) * size_t(T) * sizeof(float);
+    const void* outs[3] = {dQ, dK, dV};
+    for (int x = 0; x < 3; ++x) {
+        for (const void* p : {Q, K, V, O, dO})
+            if (overlaps(outs[x], bytes, p, bytes)) return SA_ERR_ALIAS;
+        if (overlaps(outs[x], bytes, lse, lbytes)) return SA_ERR_ALIAS;
+        for (int y = x + 1; y < 3; ++y)
+            if (overlaps(outs[x], bytes, outs[y], bytes)) return SA_ERR_ALIAS;
+    }
+    sa_mask m;
+    int rc = parse_for(spec, T, &m);
+    if (rc != SA_OK) return rc;
+    DevicePlan dp;
+    rc = cache().get(m, T, &dp);
+    if (rc != SA_OK) return rc;
+    sa::BwdDevicePlan bp;
+    rc = cache().get_bwd(m, T, &bp);
+    if (rc != SA_OK) return rc;
+    float* Dw = nullptr;
+    rc = workspace().get(lbytes, stream, &Dw);
+    if (rc != SA_OK) return rc;
+
+    sa::BwdArgs b;
+    sa::FwdArgs& a = b.f;
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.O = const_cast<void*>(O);
+    a.T = T;
+    a.BH = static_cast<int32_t>(BH);
+    a.sub = 1;
+    a.causal = m.causal;
+    a.band_back = sa::band_reach32(m);
+    a.band_fwd = m.causal ? 0 : a.band_back;
+    a.dil = m.dilation > 1 ? m.dilation : 1;
+    a.dil_pat = 0;
+    for (int x = 0; x < 64; x += a.dil) a.dil_pat |= uint64_t(1) << x;
+    a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
+    auto* base = static_cast<unsigned char*>(dp.base);
+    a.qb_order = reinterpret_cast<const int32_t*>(base + dp.off_qb_order);
+    a.run_ptr = reinterpret_cast<const int32_t*>(base + dp.off_run_ptr);
+    a.runs = reinterpret_cast<const int32_t*>(base + dp.off_runs);
+    a.gseg = reinterpret_cast<const int32_t*>(base + dp.off_gseg);
+    a.colkeys = reinterpret_cast<const int32_t*>(base + dp.off_colkeys);
+    a.colbits = reinterpret_cast<const uint64_t*>(base + dp.off_colbits);
+    a.rowbits = reinterpret_cast<const uint32_t*>(base + dp.off_rowbits);
+    a.blk = static_cast<int32_t>(m.block);
+    a.blk_ptr = reinterpret_cast<const int32_t*>(base + dp.off_blk_ptr);
+    a.blk_iv = reinterpret_cast<const int32_t*>(base + dp.off_blk_iv);
+    a.lse = nullptr;
+    b.dO = dO;
+    b.lse = lse;
+    b.dQ = dQ;
+    b.dK = dK;
+    b.dV = dV;
+    b.Dw = Dw;
+    b.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
+    auto* bb = static_cast<unsigned char*>(bp.base);
+    b.kb_order = reinterpret_cast<const int32_t*>(bb + bp.off_order);
+    b.kb_ptr = reinterpret_cast<const int32_t*>(bb + bp.off_ptr);
+    b.kb_runs = reinterpret_cast<const int32_t*>(bb + bp.off_runs);
+    b.n_kb = bp.n_kb;
+    return sa::launch_bwd(dtype, d, b, stream);
 }
 
 template <typename F>
@@ -334,6 +478,41 @@ SA_EXPORT int sparse_attn_fwd(const void* Q, const void* K, const void* V, void*
 SA_EXPORT int sparse_attn_fwd_f32(const void* Q, const void* K, const void* V, void* O, int B,
                                   int H, int T, int d, const char* mask_spec, void* stream) {
     return guarded([&] { return forward(SA_DTYPE_F32, Q, K, V, O, B, H, T, d, mask_spec, stream); });
+}
+
+SA_EXPORT int sparse_attn_fwd_lse(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                                  int B, int H, int T, int d, const char* mask_spec, void* stream) {
+    return guarded([&] {
+        if (!LSE) return SA_ERR_NULL;
+        return forward(SA_DTYPE_BF16, Q, K, V, O, B, H, T, d, mask_spec, stream, LSE);
+    });
+}
+
+SA_EXPORT int sparse_attn_fwd_lse_f32(const void* Q, const void* K, const void* V, void* O,
+                                      float* LSE, int B, int H, int T, int d, const char* mask_spec,
+                                      void* stream) {
+    return guarded([&] {
+        if (!LSE) return SA_ERR_NULL;
+        return forward(SA_DTYPE_F32, Q, K, V, O, B, H, T, d, mask_spec, stream, LSE);
+    });
+}
+
+SA_EXPORT int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* O,
+                              const void* dO, const float* LSE, void* dQ, void* dK, void* dV, int B,
+                              int H, int T, int d, const char* mask_spec, void* stream) {
+    return guarded([&] {
+        return backward(SA_DTYPE_BF16, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, T, d, mask_spec,
+                        stream);
+    });
+}
+
+SA_EXPORT int sparse_attn_bwd_f32(const void* Q, const void* K, const void* V, const void* O,
+                                  const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                                  int B, int H, int T, int d, const char* mask_spec, void* stream) {
+    return guarded([&] {
+        return backward(SA_DTYPE_F32, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, T, d, mask_spec,
+                        stream);
+    });
 }
 
 SA_EXPORT int sparse_attn_parse(const char* mask_spec, sa_mask* out) {

@@ -1,0 +1,379 @@
+// Backward pass of masked sparse attention for gfx950 (MI355X): dQ, dK, dV.
+//
+// The pages define the forward only ("Sparse attention", glossary.selfmadequant.com,
+// section "Choose the available reads": a softmax renormalised over S_i); the
+// backward is its gradient by the chain rule.  With p_ij the softmax weights
+// (recomputed from the saved log-sum-exp), dp_ij = dO_i . v_j and
+// D_i = dO_i . o_i:
+//   ds_ij = p_ij (dp_ij - D_i),  dQ_i = sum_j ds_ij k_j / sqrt(d),
+//   dK_j = sum_i ds_ij q_i / sqrt(d),  dV_j = sum_i p_ij dO_i.
+// Only allowed pairs are visited, tile by tile, as in the forward.
+//
+// Two kernels, no atomics:
+//   * sa_bwd_dq_kernel: one workgroup per (head, 128-query block), walking
+//     the forward plan (in-place key tiles, then gathered strided/global
+//     keys).  Per 64-key tile: S^T = K Q^T and dP^T = V dO^T on MFMA (keys
+//     are the MFMA rows, one query per lane column), the mask, P, dS, then
+//     dQ^T += K^T dS^T.  It also writes D_i for the second kernel.
+//   * sa_bwd_dkv_kernel: one workgroup per (head, 128-key block), walking
+//     the 64-query tiles that meet the block.  The roles swap: S = Q K^T and
+//     dP = dO V^T with queries as the MFMA rows and one key per lane column,
+//     then dV^T += dO^T P and dK^T += Q^T dS.
+// Rows go into the MFMA in the permuted order of the forward (bits 2 and 3
+// swapped) so that the 8 values a lane holds for one k-step of the second
+// product are 8 consecutive rows, read from the transposed tile at once.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.hpp"
+#include "kernel_common.hpp"
+#include "mfma_tiles.hpp"
+
+namespace sa {
+namespace {
+
+enum { BMASK_NONE = 0, BMASK_RULE = 1, BMASK_SLOTS = 2 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Fragments of 32 rows of a [T][d] tensor for this lane (row `row`, the
+// lane half's k-slices), zero past T.
+template <typename E, int D>
+__device__ __forceinline__ void load_frags(typename Ops<E>::frag* f, const E* base, int row, int T,
+                                           int h) {
+    using S = Shape<E, D>;
+#pragma unroll
+    for (int ks = 0; ks < S::NKS; ++ks) {
+        f[ks] = Ops<E>::zero();
+        if (row < T)
+            f[ks] = *reinterpret_cast<const typename Ops<E>::frag*>(base + size_t(row) * D +
+                                                                   ks * S::KSTEP + h * S::VPL);
+    }
+}
+
+// Dot product of two fragment sets (this lane's half of a row), in fp32.
+template <typename E, int D>
+__device__ __forceinline__ float frag_dot(const typename Ops<E>::frag* x,
+                                          const typename Ops<E>::frag* y) {
+    using S = Shape<E, D>;
+    float acc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < S::NKS; ++ks) {
+        if constexpr (S::VPL == 1) {
+            acc += static_cast<float>(x[ks]) * static_cast<float>(y[ks]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < S::VPL; ++e) acc += static_cast<float>(x[ks][e]) * static_cast<float>(y[ks][e]);
+        }
+    }
+    return acc;
+}
+
+// Two 32-row products of one 64-row tile: out[blk] = rows(tile) . frag^T.
+template <typename E, int D>
+__device__ __forceinline__ void tile_product(f32x16* out, const E* rows_lds,
+                                             const typename Ops<E>::frag* f, int n, int h) {
+    using S = Shape<E, D>;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        out[blk] = f32x16{};
+        const E* r = rows_lds + (blk * 32 + swap23(n)) * S::KLD + h * S::VPL;
+#pragma unroll
+        for (int ks = 0; ks < S::NKS; ++ks)
+            out[blk] = Ops<E>::mma(*reinterpret_cast<const typename Ops<E>::frag*>(r + ks * S::KSTEP),
+                                   f[ks], out[blk]);
+    }
+}
+
+// acc[db] += cols(tile)^T . x, with x the 64 tile rows held as two 32-row
+// score blocks of this lane's column (rounded to E for the MFMA).
+template <typename E, int D>
+__device__ __forceinline__ void tile_accumulate(f32x16* acc, const E* cols_lds, const f32x16* x,
+                                                int n, int h) {
+    using S = Shape<E, D>;
+    static_for<0, S::PKS>([&](auto kk_c) {
+        constexpr int kk = decltype(kk_c)::value;
+        constexpr int blk = (kk * S::VPL) >> 4;
+        constexpr int rb = (kk * S::VPL) & 15;
+        constexpr int off = blk * 32 + (rb >> 3) * 16 + (rb & 7);
+        const typename Ops<E>::frag xf = Ops<E>::template pack<rb>(x[blk]);
+#pragma unroll
+        for (int db = 0; db < S::NDB; ++db) {
+            const E* c = cols_lds + (db * 32 + n) * S::VLD + off + h * 8;
+            acc[db] = Ops<E>::mma(*reinterpret_cast<const typename Ops<E>::frag*>(c), xf, acc[db]);
+        }
+    });
+}
+
+// Tile row of score register r in block blk for lane half h.
+__device__ __forceinline__ int reg_row(int blk, int r, int h) {
+    return blk * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
+}
+
+// Store a d x 32 accumulator (row = d index, column = this lane's row) times
+// `mul` into row `row` of a [T][d] tensor.
+template <typename E, int D>
+__device__ __forceinline__ void store_rows(E* dst, const f32x16* acc, int row, int h, float mul) {
+    using S = Shape<E, D>;
+#pragma unroll
+    for (int db = 0; db < S::NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d0 = db * 32 + g * 8 + h * 4;
+            if (d0 < D) {
+                typename Ops<E>::quad q;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) q[e] = static_cast<E>(acc[db][g * 4 + e] * mul);
+                *reinterpret_cast<typename Ops<E>::quad*>(dst + size_t(row) * D + d0) = q;
+            }
+        }
+}
+
+// ---------------------------------------------------------------- dQ kernel
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void sa_bwd_dq_kernel(BwdArgs b) {
+    using S = Shape<E, D>;
+    using F = typename Ops<E>::frag;
+    const FwdArgs& a = b.f;
+    __shared__ __attribute__((aligned(16))) E k_lds[kBK * S::KLD];
+    __shared__ __attribute__((aligned(16))) E v_lds[kBK * S::KLD];
+    __shared__ __attribute__((aligned(16))) E kt_lds[S::VROWS * S::VLD];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, h = lane >> 5;
+    const int work = xcd_slice_index(blockIdx.x, gridDim.x);
+    const int n_qb = gridDim.x / a.BH;
+    const int bh = work / n_qb;
+    const int qb = a.qb_order[work % n_qb];
+    const int T = a.T;
+    const size_t base = size_t(bh) * size_t(T) * D;
+    const E* Qp = static_cast<const E*>(a.Q) + base;
+    const E* Kp = static_cast<const E*>(a.K) + base;
+    const E* Vp = static_cast<const E*>(a.V) + base;
+    const E* Op = static_cast<const E*>(a.O) + base;
+    const E* Gp = static_cast<const E*>(b.dO) + base;
+    const int qi = qb * kBQ + wave * 32 + n;
+
+    if (D < 32) {  // rows of the transposed tile past d stay zero
+        for (int x = tid; x < (S::VROWS - D) * S::VLD; x += kThreads)
+            kt_lds[D * S::VLD + x] = static_cast<E>(0.f);
+    }
+
+    F qf[S::NKS], gf[S::NKS];
+    load_frags<E, D>(qf, Qp, qi, T, h);
+    load_frags<E, D>(gf, Gp, qi, T, h);
+    float Dq;
+    {
+        F of[S::NKS];
+        load_frags<E, D>(of, Op, qi, T, h);
+        const float part = frag_dot<E, D>(gf, of);
+        Dq = part + __shfl_xor(part, 32);
+    }
+    if (qi < T && h == 0) b.Dw[size_t(bh) * size_t(T) + size_t(qi)] = Dq;
+    const float lse2 = qi < T ? b.lse[size_t(bh) * size_t(T) + size_t(qi)] * kLog2e : 0.f;
+    const bool rowg = qi < T && ((a.rowbits[qi >> 5] >> (qi & 31)) & 1u);
+    const int qres = a.dil == 1 ? 0 : qi % a.dil;
+    const int qblk = a.blk > 0 ? min(qi, T - 1) / a.blk : 0;
+
+    f32x16 acc[S::NDB];
+#pragma unroll
+    for (int db = 0; db < S::NDB; ++db) acc[db] = f32x16{};
+
+    auto tile = [&](int mode, int k0, int cnt) {
+        f32x16 s[2], dp[2];
+        tile_product<E, D>(s, k_lds, qf, n, h);
+        tile_product<E, D>(dp, v_lds, gf, n, h);
+        uint64_t aw = ~0ull;
+        if (mode == BMASK_RULE)
+            aw = allowed_word(a, qi, k0, rowg, a.colbits[k0 >> 6], qres,
+                              a.dil == 1 ? 0 : k0 % a.dil, qblk);
+        else if (mode == BMASK_SLOTS)
+            aw = low_bits(cnt);
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const bool ok = (aw >> reg_row(blk, r, h)) & 1;
+                const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[blk][r], a.scale_log2, -lse2)) : 0.f;
+                s[blk][r] = p * (dp[blk][r] - Dq);  // dS
+            }
+        tile_accumulate<E, D>(acc, kt_lds, s, n, h);
+    };
+
+    // In-place key tiles, run by run.
+    for (int r = a.run_ptr[qb]; r < a.run_ptr[qb + 1]; ++r) {
+        const int kb0 = a.runs[2 * r];
+        const int w1 = a.runs[2 * r + 1];
+        const int kb1 = w1 & 0x7fffffff;
+        const bool masked = w1 < 0;
+        for (int kb = kb0; kb < kb1; ++kb) {
+            const int k0 = kb * kBK;
+            auto key_of = [&](int row) { return k0 + row < T ? k0 + row : -1; };
+            __syncthreads();
+            stage_rows<E, D>(k_lds, Kp, key_of, tid);
+            stage_rows<E, D>(v_lds, Vp, key_of, tid);
+            stage_cols<E, D>(kt_lds, Kp, key_of, tid);
+            __syncthreads();
+            tile(masked ? BMASK_RULE : BMASK_NONE, k0, kBK);
+        }
+    }
+    // Gathered strided/global keys.
+    {
+        const int a0 = a.gseg[4 * qb], a1 = a.gseg[4 * qb + 1];
+        const int b0 = a.gseg[4 * qb + 2], b1 = a.gseg[4 * qb + 3];
+        const int na = a1 - a0, total = na + (b1 - b0);
+        for (int g = 0; g < total; g += kBK) {
+            const int cnt = min(kBK, total - g);
+            auto key_of = [&](int row) {
+                const int sl = g + row;
+                if (row >= cnt) return -1;
+                return a.colkeys[sl < na ? a0 + sl : b0 + (sl - na)];
+            };
+            __syncthreads();
+            stage_rows<E, D>(k_lds, Kp, key_of, tid);
+            stage_rows<E, D>(v_lds, Vp, key_of, tid);
+            stage_cols<E, D>(kt_lds, Kp, key_of, tid);
+            __syncthreads();
+            tile(BMASK_SLOTS, 0, cnt);
+        }
+    }
+    if (qi < T) store_rows<E, D>(static_cast<E*>(b.dQ) + base, acc, qi, h, b.scale);
+}
+
+// -------------------------------------------------------------- dK/dV kernel
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void sa_bwd_dkv_kernel(BwdArgs b) {
+    using S = Shape<E, D>;
+    using F = typename Ops<E>::frag;
+    const FwdArgs& a = b.f;
+    static_assert(kBKB == kWaves * 32, "one 32-key MFMA column block per wave");
+    static_assert(kBQB == kBK, "query tiles use the 64-row tile geometry");
+    __shared__ __attribute__((aligned(16))) E q_lds[kBQB * S::KLD];
+    __shared__ __attribute__((aligned(16))) E g_lds[kBQB * S::KLD];
+    __shared__ __attribute__((aligned(16))) E qt_lds[S::VROWS * S::VLD];
+    __shared__ __attribute__((aligned(16))) E gt_lds[S::VROWS * S::VLD];
+    __shared__ __attribute__((aligned(16))) float lse_s[kBQB];
+    __shared__ __attribute__((aligned(16))) float d_s[kBQB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, h = lane >> 5;
+    const int work = xcd_slice_index(blockIdx.x, gridDim.x);
+    const int bh = work / b.n_kb;
+    const int kb = b.kb_order[work % b.n_kb];
+    const int T = a.T;
+    const size_t base = size_t(bh) * size_t(T) * D;
+    const E* Qp = static_cast<const E*>(a.Q) + base;
+    const E* Kp = static_cast<const E*>(a.K) + base;
+    const E* Vp = static_cast<const E*>(a.V) + base;
+    const E* Gp = static_cast<const E*>(b.dO) + base;
+    const float* Lp = b.lse + size_t(bh) * size_t(T);
+    const float* Dp = b.Dw + size_t(bh) * size_t(T);
+    const int kj = kb * kBKB + wave * 32 + n;  // this lane's key
+
+    if (D < 32) {
+        for (int x = tid; x < (S::VROWS - D) * S::VLD; x += kThreads) {
+            qt_lds[D * S::VLD + x] = static_cast<E>(0.f);
+            gt_lds[D * S::VLD + x] = static_cast<E>(0.f);
+        }
+    }
+
+    F kf[S::NKS], vf[S::NKS];
+    load_frags<E, D>(kf, Kp, kj, T, h);
+    load_frags<E, D>(vf, Vp, kj, T, h);
+    const bool colj = kj < T && ((a.colbits[kj >> 6] >> (kj & 63)) & 1);
+
+    f32x16 dk[S::NDB], dv[S::NDB];
+#pragma unroll
+    for (int db = 0; db < S::NDB; ++db) dk[db] = dv[db] = f32x16{};
+
+    for (int r = b.kb_ptr[kb]; r < b.kb_ptr[kb + 1]; ++r) {
+        const int qt0 = b.kb_runs[2 * r];
+        const int w1 = b.kb_runs[2 * r + 1];
+        const int qt1 = w1 & 0x7fffffff;
+        const bool masked = w1 < 0;
+        for (int qt = qt0; qt < qt1; ++qt) {
+            const int q0 = qt * kBQB;
+            auto row_of = [&](int row) { return q0 + row < T ? q0 + row : -1; };
+            __syncthreads();
+            stage_rows<E, D>(q_lds, Qp, row_of, tid);
+            stage_rows<E, D>(g_lds, Gp, row_of, tid);
+            stage_cols<E, D>(qt_lds, Qp, row_of, tid);
+            stage_cols<E, D>(gt_lds, Gp, row_of, tid);
+            if (tid < kBQB) {
+                const int i = q0 + tid;
+                lse_s[tid] = i < T ? Lp[i] * kLog2e : 0.f;
+                d_s[tid] = i < T ? Dp[i] : 0.f;
+            }
+            __syncthreads();
+
+            f32x16 s[2], dp[2];
+            tile_product<E, D>(s, q_lds, kf, n, h);
+            tile_product<E, D>(dp, g_lds, vf, n, h);
+            uint64_t aw = ~0ull;
+            if (masked) {
+                uint64_t roww = 0;
+                const int w0 = q0 >> 5, nw = (T + 31) >> 5;
+                if (w0 < nw) roww = a.rowbits[w0];
+                if (w0 + 1 < nw) roww |= uint64_t(a.rowbits[w0 + 1]) << 32;
+                aw = kj < T ? allowed_word_T(a, kj, q0, colj, roww) : 0ull;
+            }
+            f32x16 p[2];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int r4 = 0; r4 < 16; r4 += 4) {
+                    const int x0 = reg_row(blk, r4, h);  // 4 consecutive rows
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + x0);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(d_s + x0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool ok = (aw >> (x0 + e)) & 1;
+                        const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[blk][r4 + e], a.scale_log2, -l4[e])) : 0.f;
+                        p[blk][r4 + e] = pv;
+                        s[blk][r4 + e] = pv * (dp[blk][r4 + e] - d4[e]);  // dS
+                    }
+                }
+            tile_accumulate<E, D>(dv, gt_lds, p, n, h);
+            tile_accumulate<E, D>(dk, qt_lds, s, n, h);
+        }
+    }
+    if (kj < T) {
+        store_rows<E, D>(static_cast<E*>(b.dK) + base, dk, kj, h, b.scale);
+        store_rows<E, D>(static_cast<E*>(b.dV) + base, dv, kj, h, 1.f);
+    }
+}
+
+template <typename E, int D>
+int launch_b(const BwdArgs& b, void* stream) {
+    const unsigned g1 = static_cast<unsigned>(int64_t(b.f.BH) * ((b.f.T + kBQ - 1) / kBQ));
+    hipLaunchKernelGGL((sa_bwd_dq_kernel<E, D>), dim3(g1), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), b);
+    if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
+    const unsigned g2 = static_cast<unsigned>(int64_t(b.f.BH) * b.n_kb);
+    hipLaunchKernelGGL((sa_bwd_dkv_kernel<E, D>), dim3(g2), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), b);
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+}  // namespace
+
+int launch_bwd(int dtype, int d, const BwdArgs& b, void* stream) {
+    if (dtype == SA_DTYPE_BF16) {
+        switch (d) {
+            case 16: return launch_b<__bf16, 16>(b, stream);
+            case 32: return launch_b<__bf16, 32>(b, stream);
+            case 64: return launch_b<__bf16, 64>(b, stream);
+            case 128: return launch_b<__bf16, 128>(b, stream);
+        }
+    } else if (dtype == SA_DTYPE_F32) {
+        switch (d) {
+            case 16: return launch_b<float, 16>(b, stream);
+            case 32: return launch_b<float, 32>(b, stream);
+            case 64: return launch_b<float, 64>(b, stream);
+            case 128: return launch_b<float, 128>(b, stream);
+        }
+    }
+    return SA_ERR_UNSUPPORTED;
+}
+
+}  // namespace sa

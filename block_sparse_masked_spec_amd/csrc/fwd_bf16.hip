@@ -393,6 +393,12 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
                                                          __float_as_uint(st.l_run[g]), false, false);
         const float lt = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
         const float inv = 1.f / lt;
+        if (a.lse && qi < T && h == 0) {  // log-sum-exp: the scores are in log2 units
+            const size_t row = SUB ? size_t(bh / a.sub) * size_t(T) * a.sub + size_t(bh % a.sub) +
+                                         size_t(qi) * a.sub
+                                   : size_t(bh) * size_t(T) + size_t(qi);
+            a.lse[row] = (st.m_run[g] + __log2f(lt)) * 0.6931471805599453f;
+        }
         if (qi < T) {
 #pragma unroll
             for (int db = 0; db < L::NDB; ++db)

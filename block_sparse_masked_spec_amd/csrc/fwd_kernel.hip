@@ -32,124 +32,12 @@
 
 #include "internal.hpp"
 #include "kernel_common.hpp"
+#include "mfma_tiles.hpp"
 
 namespace sa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-static_assert(kBQ == kWaves * 32, "one 32-query MFMA column block per wave");
-static_assert(kBK == 64, "column bit words cover exactly one key tile");
-
 enum { MASK_NONE = 0, MASK_RULE = 1, MASK_SLOTS = 2 };
-
-// Per element type: MFMA flavour, lane fragment and 16-byte chunk views.
-template <typename E>
-struct Ops;
-
-template <>
-struct Ops<__bf16> {
-    static constexpr int VPL = 8;  // elements per lane per MFMA k-step
-    using frag = bf16x8;
-    using chunk = bf16x8;  // one 16-byte global chunk
-    using quad = bf16x4;   // 4 keys of one transposed V row
-    __device__ static f32x16 mma(frag a, frag b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    // Scores rb .. rb+7 of one 32-key block as a B fragment.
-    template <int RB>
-    __device__ static frag pack(const f32x16& s) {
-        frag r;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = static_cast<__bf16>(s[RB + e]);
-        return r;
-    }
-    __device__ static frag zero() { return frag{}; }
-};
-
-template <>
-struct Ops<float> {
-    static constexpr int VPL = 1;
-    using frag = float;
-    using chunk = f32x4;
-    using quad = f32x4;
-    __device__ static f32x16 mma(frag a, frag b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-    }
-    template <int RB>
-    __device__ static frag pack(const f32x16& s) {
-        return s[RB];
-    }
-    __device__ static frag zero() { return 0.f; }
-};
-
-template <typename E, int D>
-struct Shape {
-    static constexpr int EPC = 16 / sizeof(E);        // elements per 16-byte chunk
-    static constexpr int CPR = D / EPC;               // chunks per K/V row
-    static constexpr int KLD = D + EPC;               // K row stride (16-byte pad)
-    static constexpr int NDB = D >= 32 ? D / 32 : 1;  // 32-row blocks of d
-    static constexpr int VROWS = NDB * 32;            // rows of the V^T tile
-    static constexpr int VLD = kBK + EPC;             // V^T row stride (16-byte pad)
-    static constexpr int VPL = Ops<E>::VPL;
-    static constexpr int KSTEP = 2 * VPL;             // MFMA k per instruction
-    static constexpr int NKS = D / KSTEP;             // k-steps of S^T = K Q^T
-    static constexpr int PKS = kBK / KSTEP;           // k-steps of O^T += V^T P^T
-};
-
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, N>(f);
-    }
-}
-
-// MFMA row m of a 32-key block holds key swap23(m) of that block.
-__device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
-
-// Stage one 64-key tile: K row-major, V transposed.  key_of(row) gives the
-// key index of tile row `row`, or -1 for an unused row (filled with zeros).
-template <typename E, int D, typename KeyOf>
-__device__ __forceinline__ void stage(E* k_lds, E* vt_lds, const E* Kp, const E* Vp,
-                                      KeyOf key_of, int tid) {
-    using S = Shape<E, D>;
-    using chunk = typename Ops<E>::chunk;
-    using quad = typename Ops<E>::quad;
-#pragma unroll
-    for (int c = tid; c < kBK * S::CPR; c += kThreads) {
-        const int row = c / S::CPR, col = c % S::CPR;
-        const int key = key_of(row);
-        chunk v{};
-        if (key >= 0) v = *reinterpret_cast<const chunk*>(Kp + size_t(key) * D + col * S::EPC);
-        *reinterpret_cast<chunk*>(k_lds + row * S::KLD + col * S::EPC) = v;
-    }
-#pragma unroll
-    for (int b = tid; b < (kBK / 4) * S::CPR; b += kThreads) {
-        const int rg = b % (kBK / 4), col = b / (kBK / 4);
-        chunk x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = key_of(rg * 4 + i);
-            x[i] = chunk{};
-            if (key >= 0) x[i] = *reinterpret_cast<const chunk*>(Vp + size_t(key) * D + col * S::EPC);
-        }
-#pragma unroll
-        for (int e = 0; e < S::EPC; ++e) {
-            quad q;
-            q[0] = x[0][e];
-            q[1] = x[1][e];
-            q[2] = x[2][e];
-            q[3] = x[3][e];
-            *reinterpret_cast<quad*>(vt_lds + (col * S::EPC + e) * S::VLD + rg * 4) = q;
-        }
-    }
-}
 
 template <typename E, int D>
 struct WaveState {
@@ -314,6 +202,8 @@ __global__ __launch_bounds__(kThreads) void sa_fwd_kernel(FwdArgs a) {
     // Epilogue: O = acc / l, both lane halves' sums combined.
     const float lt = st.l_run + __shfl_xor(st.l_run, 32);
     const float inv = 1.f / lt;
+    if (a.lse && qi < T && h == 0)  // log-sum-exp: the scores are in log2 units
+        a.lse[size_t(bh) * size_t(T) + size_t(qi)] = (st.m_run + __log2f(lt)) * 0.6931471805599453f;
     if (qi < T) {
 #pragma unroll
         for (int db = 0; db < S::NDB; ++db)

@@ -118,6 +118,14 @@ struct DevicePlan {
            off_colbits = 0, off_rowbits = 0, off_blk_ptr = 0, off_blk_iv = 0;
 };
 
+// Device-resident backward plan (one allocation).
+struct BwdDevicePlan {
+    void* base = nullptr;
+    size_t bytes = 0;
+    int32_t n_kb = 0;
+    size_t off_order = 0, off_ptr = 0, off_runs = 0;
+};
+
 // Kernel arguments (passed by value).
 struct FwdArgs {
     const void* Q;
@@ -148,10 +156,45 @@ struct FwdArgs {
     const int32_t* colkeys;
     const uint64_t* colbits;
     const uint32_t* rowbits;
+    float* lse;  // optional [BH][T] output: natural-log sum of exp of the row's scores
 };
 
 constexpr int kBQ = 128;
 constexpr int kBK = 64;
+
+// Backward plan: for each block of kBKB keys, runs of the kBQB-query tiles
+// that hold allowed pairs with it (the forward plan read by key).
+constexpr int kBKB = 128;  // keys per dK/dV workgroup
+constexpr int kBQB = 64;   // queries per tile it visits
+
+struct BwdHostPlan {
+    int32_t n_kb = 0, n_qt = 0;
+    std::vector<int32_t> kb_order;  // key blocks, most work first
+    std::vector<int32_t> kb_ptr;    // n_kb + 1
+    std::vector<int32_t> kb_runs;   // pairs: qt_begin, qt_end | (needs_mask << 31)
+    int64_t tiles = 0, masked_tiles = 0;
+};
+
+BwdHostPlan build_bwd_plan(const MaskRule& rule);
+
+// Backward arguments: the forward's (rule, plan, Q, K, V, O) plus gradients,
+// the saved log-sum-exp and the transposed plan.
+struct BwdArgs {
+    FwdArgs f;           // f.Q, f.K, f.V, f.O, rule and forward plan; f.lse unused
+    const void* dO;      // [BH][T][d]
+    const float* lse;    // [BH][T] natural-log sum of exp, from the forward
+    void* dQ;            // [BH][T][d] outputs, input dtype
+    void* dK;
+    void* dV;
+    float* Dw;           // [BH][T] workspace: D_i = dO_i . O_i
+    float scale;         // 1 / sqrt(d)
+    const int32_t* kb_order;
+    const int32_t* kb_ptr;
+    const int32_t* kb_runs;
+    int32_t n_kb;
+};
+
+int launch_bwd(int dtype, int d, const BwdArgs& args, void* stream);
 
 // Decode arguments (passed by value): n_new query tokens per sequence against
 // ring-buffer caches [B][Hkv][C][d]; position t lives in slot t mod C.

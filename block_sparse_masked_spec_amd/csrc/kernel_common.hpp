@@ -73,4 +73,39 @@ __device__ __forceinline__ uint64_t allowed_word(const FwdArgs& a, int qi, int k
     return w;
 }
 
+// The same rule read by key: bit x is set iff query q0 + x may read key j.
+// colj: key j is a strided or global column key; roww: bit x set iff query
+// q0 + x is a global row.
+__device__ __forceinline__ uint64_t allowed_word_T(const FwdArgs& a, int j, int q0, bool colj,
+                                                   uint64_t roww) {
+    uint64_t w = colj ? ~0ull : roww;
+    if (!colj) {
+        // band: i - j in [-fwd, back], i.e. x in [j - fwd - q0, j + back - q0]
+        const long lo = long(j) - a.band_fwd - q0;
+        const long hi = long(j) + long(a.band_back) - q0 + 1;
+        if (hi > 0 && lo < 64) {
+            const int l0 = lo < 0 ? 0 : int(lo), h0 = hi > 64 ? 64 : int(hi);
+            uint64_t band = low_bits(h0) & ~low_bits(l0);
+            if (a.dil != 1) band &= grid_word(a.dil_pat, a.dil, j % a.dil, q0 % a.dil);
+            w |= band;
+        }
+        if (a.blk > 0) {  // query blocks of the tile whose intervals hold key block j / blk
+            const int kbj = j / a.blk;
+            const int qe = min(q0 + 64, a.T);
+            for (int qb = q0 / a.blk; qb * a.blk < qe; ++qb) {
+                bool hit = false;
+                for (int t = a.blk_ptr[qb]; t < a.blk_ptr[qb + 1]; ++t)
+                    hit |= a.blk_iv[2 * t] <= kbj && kbj < a.blk_iv[2 * t + 1];
+                if (hit) {
+                    const int l0 = max(qb * a.blk, q0) - q0, h0 = min((qb + 1) * a.blk, qe) - q0;
+                    w |= low_bits(h0) & ~low_bits(l0);
+                }
+            }
+        }
+    }
+    w &= low_bits(a.T - q0);
+    if (a.causal) w &= ~low_bits(j - q0);  // i >= j
+    return w;
+}
+
 }  // namespace sa

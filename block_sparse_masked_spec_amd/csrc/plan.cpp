@@ -244,4 +244,57 @@ HostPlan build_plan(const MaskRule& rule, int32_t bq, int32_t bk) {
     return p;
 }
 
+BwdHostPlan build_bwd_plan(const MaskRule& rule) {
+    BwdHostPlan p;
+    const int64_t T = rule.T();
+    p.n_kb = static_cast<int32_t>((T + kBKB - 1) / kBKB);
+    p.n_qt = static_cast<int32_t>((T + kBQB - 1) / kBQB);
+    const bool any_global_row = rule.rows_global_in(0, T) > 0;
+    const int64_t back = rule.band_back(), fwd = rule.band_fwd();
+    std::vector<int64_t> work(p.n_kb, 0);
+    p.kb_ptr.push_back(0);
+    for (int32_t kb = 0; kb < p.n_kb; ++kb) {
+        const int64_t k0 = int64_t(kb) * kBKB, k1 = std::min<int64_t>(T, k0 + kBKB);
+        // Query tiles that can hold allowed pairs: every tile when some row is
+        // global, the block has column keys or in block mode; else the rows
+        // whose band meets the block.
+        int64_t qlo = 0, qhi = T - 1;
+        if (!any_global_row && rule.col_keys_in(k0, k1) == 0 && rule.block() == 0) {
+            qlo = fwd >= T ? 0 : std::max<int64_t>(0, k0 - fwd);
+            qhi = back >= T ? T - 1 : std::min<int64_t>(T - 1, k1 - 1 + back);
+            if (rule.causal()) qlo = std::max(qlo, k0);
+        }
+        bool open = false;
+        int64_t tiles = 0;
+        for (int64_t qt = qlo / kBQB; qt <= qhi / kBQB && qt < p.n_qt; ++qt) {
+            const int64_t q0 = qt * kBQB, q1 = std::min<int64_t>(T, q0 + kBQB);
+            const int cls = rule.classify(q0, q1, k0, k1);
+            if (cls == SA_TILE_EMPTY) {
+                open = false;
+                continue;
+            }
+            const bool need_mask = !(cls == SA_TILE_FULL && q0 + kBQB <= T && k0 + kBKB <= T);
+            const int32_t flag = need_mask ? int32_t(0x80000000u) : 0;
+            if (open && (p.kb_runs.back() & int32_t(0x80000000u)) == flag &&
+                (p.kb_runs.back() & 0x7fffffff) == qt) {
+                p.kb_runs.back() = int32_t(qt + 1) | flag;
+            } else {
+                p.kb_runs.push_back(static_cast<int32_t>(qt));
+                p.kb_runs.push_back(int32_t(qt + 1) | flag);
+                open = true;
+            }
+            ++tiles;
+            p.masked_tiles += need_mask ? 1 : 0;
+        }
+        p.kb_ptr.push_back(static_cast<int32_t>(p.kb_runs.size() / 2));
+        p.tiles += tiles;
+        work[kb] = tiles;
+    }
+    p.kb_order.resize(p.n_kb);
+    std::iota(p.kb_order.begin(), p.kb_order.end(), 0);
+    std::stable_sort(p.kb_order.begin(), p.kb_order.end(),
+                     [&](int32_t x, int32_t y) { return work[x] > work[y]; });
+    return p;
+}
+
 }  // namespace sa

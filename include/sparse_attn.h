@@ -162,6 +162,42 @@ int sparse_attn_fwd_f32(const void* Q, const void* K, const void* V, void* O,
                         int B, int H, int T, int d, const char* mask_spec,
                         void* stream);
 
+/*
+ * Forward that also writes LSE: device float [B][H][T], the natural-log
+ * log-sum-exp of each row's allowed scores, lse_i = log sum_{j in S_i}
+ * exp(Q_i.K_j / sqrt(d)) (what the backward needs to rebuild the weights).
+ * Otherwise as sparse_attn_fwd / sparse_attn_fwd_f32; LSE must be 4-byte
+ * aligned and must not overlap Q, K, V or O (SA_ERR_ALIAS).
+ */
+int sparse_attn_fwd_lse(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                        int B, int H, int T, int d, const char* mask_spec, void* stream);
+int sparse_attn_fwd_lse_f32(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            int B, int H, int T, int d, const char* mask_spec, void* stream);
+
+/*
+ * Backward pass: gradients of the forward for an upstream gradient dO.  The
+ * pages define the forward only; this is its gradient by the chain rule
+ * through the softmax over S_i ("Sparse attention", "Choose the available
+ * reads").  With p_ij = exp(Q_i.K_j / sqrt(d) - LSE_i) for j in S_i,
+ * dp_ij = dO_i.V_j, D_i = dO_i.O_i and ds_ij = p_ij (dp_ij - D_i):
+ *   dQ_i = sum_j ds_ij K_j / sqrt(d),  dK_j = sum_i ds_ij Q_i / sqrt(d),
+ *   dV_j = sum_i p_ij dO_i.
+ * Q, K, V, O, dO (input dtype: bf16 for sparse_attn_bwd, fp32 for _f32) and
+ * LSE (float) are the forward's tensors and its LSE output for the same
+ * mask_spec; dQ, dK, dV are written in full ([B][H][T][d], input dtype).
+ * Outputs must not overlap each other or any input (SA_ERR_ALIAS).  A
+ * library-owned fp32 workspace of B*H*T floats per (device, stream) holds
+ * D between the two kernels (shared with decode, grown on demand).
+ * Returns SA_OK or SA_ERR_{NULL, SHAPE, UNSUPPORTED, ALIGN, ALIAS, SPEC,
+ * RANGE, NOMEM, HIP}, validation before any device work.
+ */
+int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                    const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int T, int d,
+                    const char* mask_spec, void* stream);
+int sparse_attn_bwd_f32(const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const float* LSE, void* dQ, void* dK, void* dV, int B,
+                        int H, int T, int d, const char* mask_spec, void* stream);
+
 /* Parse mask_spec into *out (host only).  SA_ERR_SPEC on any grammar
  * error, SA_ERR_NULL on NULL arguments. */
 int sparse_attn_parse(const char* mask_spec, sa_mask* out);

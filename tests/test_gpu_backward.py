@@ -1,0 +1,127 @@
+"""GPU parity of the forward's log-sum-exp output and of the backward pass
+(dQ, dK, dV) against the fp64 oracle.
+
+Tolerances:
+* LSE (fp32 output): |lse - lse*| <= 1e-4 for fp32 inputs (scores and sums
+  in fp32); <= 2^-8 for bf16, where the fast forward sums the weights after
+  rounding them to bf16 (each within 2^-9 relative, so log l moves by at most
+  about 2^-9) -- the same weights that multiply V and normalise O.
+* fp32 gradients: max |g - g*| <= 1e-4 * max(1, max |g*|) per tensor (the
+  floor covers gradients that vanish exactly, like T = 1, where the terms
+  are O(1) with N(0,1) inputs), and per row <= 1e-3 of that row's max.  The weights are rebuilt from the fp32 LSE
+  (relative error a few fp32 ulps times the score magnitude, about 1e-6) and
+  the products accumulate in fp32; a row of dQ or dK is a sum whose
+  coefficients ds_ij sum to zero, so a row with a small gradient keeps the
+  absolute error of its larger terms and its own relative error grows.
+* bf16 gradients: max |g - g*| <= 3e-2 * max(1, max |g*|) per tensor.  The
+  MFMA operands P and dS are rounded to bf16 (relative 2^-9 each), the
+  outputs too, and a key's gradient sums up to T such terms.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_masked_spec_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+SPECS = [
+    "causal",
+    "causal;window=7",
+    "causal;window=100;stride=32;phase=5",
+    "causal;window=3;stride=5;global=0,77:80",
+    "bidir",
+    "bidir;radius=40;stride=16",
+    "bidir;radius=5;global=0:3,150,299",
+    "causal;window=9;dilation=2",
+    "blocks;block=64;radius=1;random=3;seed=0;global=0:8",
+]
+
+
+def announce(msg):
+    sys.__stderr__.write(f"[gpu] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def run(gpu, spec, q, k, v, g):
+    """Forward with LSE, then backward, on the GPU; returns CPU tensors."""
+    B, H, T, d = q.shape
+    announce(f"bwd {q.dtype} B={B} H={H} T={T} d={d} spec={spec}")
+    qd, kd, vd, gd = (x.cuda() for x in (q, k, v, g))
+    od = torch.empty_like(qd)
+    lse = torch.empty(B, H, T, dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(qd), torch.empty_like(qd)
+    if q.dtype == torch.bfloat16:
+        gpu.sparse_attn_fwd_lse(qd, kd, vd, od, lse, B, H, T, d, spec)
+        gpu.sparse_attn_bwd(qd, kd, vd, od, gd, lse, dq, dk, dv, B, H, T, d, spec)
+    else:
+        gpu.sparse_attn_fwd_lse_f32(qd, kd, vd, od, lse, B, H, T, d, spec)
+        gpu.sparse_attn_bwd_f32(qd, kd, vd, od, gd, lse, dq, dk, dv, B, H, T, d, spec)
+    torch.cuda.synchronize()
+    return od.cpu(), lse.cpu(), dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def check_grad(got, ref, dtype, what):
+    g = got.double().numpy()
+    assert np.isfinite(g).all(), f"non-finite {what}"
+    if dtype == "bf16":
+        tol = 3e-2 * max(1.0, np.abs(ref).max())
+        err = np.abs(g - ref).max()
+        assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.3e}"
+        return err / tol
+    err = np.abs(g - ref).max()
+    assert err <= 1e-4 * max(1.0, np.abs(ref).max()), f"{what}: max abs err {err:.3e}"
+    g2, r2 = g.reshape(-1, g.shape[-1]), ref.reshape(-1, ref.shape[-1])
+    scale = np.maximum(np.abs(r2).max(-1), 1e-30)
+    rowrel = (np.abs(g2 - r2).max(-1) / scale)
+    rowrel = rowrel[np.abs(r2).max(-1) > 1e-3].max(initial=0.0)
+    assert rowrel <= 1e-3, f"{what}: row-normwise rel err {rowrel:.3e}"
+    return rowrel
+
+
+def full_check(gpu, spec, B, H, T, d, dtype, seed):
+    q, k, v = inputs.qkv(B, H, T, d, dtype, seed)
+    g = inputs.qkv(B, H, T, d, dtype, seed + 500)[0]
+    o, lse, dq, dk, dv = run(gpu, spec, q, k, v, g)
+    _, lse_ref, _ = oracle.forward_rows(spec, q, k, v)
+    lse_tol = 2.0 ** -8 if dtype == "bf16" else 1e-4
+    assert np.abs(lse.double().numpy() - lse_ref).max() <= lse_tol, f"lse {spec}"
+    # the backward's upstream inputs are the GPU's own O (as in training)
+    rq, rk, rv = oracle.backward(spec, q, k, v, g)
+    worst = 0.0
+    for got, ref, nm in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+        worst = max(worst, check_grad(got, ref, dtype, f"{nm} {spec} T={T} d={d} {dtype}"))
+    return worst
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("spec", SPECS)
+def test_backward_small_ragged(gpu, spec, d, dtype):
+    """T=300: 3 query blocks, 3 key blocks of the dK/dV pass, ragged tails."""
+    full_check(gpu, spec, 2, 2, 300, d, dtype, seed=zlib.crc32(f"{spec}/{d}".encode()) % 1000)
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 128, 129, 257])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_edge_lengths(gpu, T, dtype):
+    for spec in ["causal;window=5;stride=7", "bidir;radius=9;global=0"]:
+        full_check(gpu, spec, 1, 2, T, 64, dtype, seed=T)
+
+
+def test_backward_window_layer_2k(gpu):
+    """B=1, H=4, T=2048, d=128, causal window 256: every gradient compared."""
+    full_check(gpu, "causal;window=256", 1, 4, 2048, 128, "bf16", seed=3)
+
+
+def test_backward_is_deterministic(gpu):
+    q, k, v = inputs.qkv(1, 4, 1024, 128, "bf16", 4)
+    g = inputs.qkv(1, 4, 1024, 128, "bf16", 5)[0]
+    a = run(gpu, "causal;window=200;stride=64", q, k, v, g)
+    b = run(gpu, "causal;window=200;stride=64", q, k, v, g)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

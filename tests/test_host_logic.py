@@ -360,3 +360,32 @@ def test_decode_rejects_bad_arguments_before_any_device_work():
     assert call(Q=Q + 8) == sa.SA_ERR_ALIGN
     assert call(pos=P + 2) == sa.SA_ERR_ALIGN
     assert call(O=K + 64) == sa.SA_ERR_ALIAS
+
+
+def test_backward_rejects_bad_arguments_before_any_device_work():
+    lib = sa.load()
+    Q, K, V, O, G, L, dQ, dK, dV = (0x100000 * (i + 1) for i in range(9))
+    bwd = lib.sparse_attn_bwd
+    names = ["Q", "K", "V", "O", "dO", "LSE", "dQ", "dK", "dV", "B", "H", "T", "d", "spec"]
+    ok = [Q, K, V, O, G, L, dQ, dK, dV, 1, 2, 64, 64, b"causal;window=8"]
+
+    def call(**kw):
+        args = list(ok)
+        for key, val in kw.items():
+            args[names.index(key)] = val
+        return bwd(*args, None)
+
+    assert call(dO=None) == sa.SA_ERR_NULL
+    assert call(LSE=None) == sa.SA_ERR_NULL
+    assert call(T=0) == sa.SA_ERR_SHAPE
+    assert call(d=48) == sa.SA_ERR_UNSUPPORTED
+    assert call(dK=dK + 8) == sa.SA_ERR_ALIGN
+    assert call(LSE=L + 2) == sa.SA_ERR_ALIGN
+    assert call(dQ=Q) == sa.SA_ERR_ALIAS
+    assert call(dV=dK + 16) == sa.SA_ERR_ALIAS
+    assert call(dK=L) == sa.SA_ERR_ALIAS
+    assert call(spec=b"causal;window=") == sa.SA_ERR_SPEC
+    assert call(spec=b"causal;global=64") == sa.SA_ERR_RANGE
+    fl = lib.sparse_attn_fwd_lse
+    assert fl(Q, K, V, O, None, 1, 2, 64, 64, b"causal", None) == sa.SA_ERR_NULL
+    assert fl(Q, K, V, O, O + 16, 1, 2, 64, 64, b"causal", None) == sa.SA_ERR_ALIAS
