@@ -31,7 +31,8 @@ BF16_PEAK_TFLOPS = 2500.0
 F32_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_masked_spec_amd", "csrc", f)
-               for f in ("fwd_kernel.hip", "fwd_bf16.hip", "decode.hip", "internal.hpp")]
+               for f in ("fwd_kernel.hip", "fwd_bf16.hip", "decode.hip", "bwd_kernel.hip",
+                         "mfma_tiles.hpp", "kernel_common.hpp", "internal.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = {
@@ -47,6 +48,8 @@ WORKLOADS = {
                                specs=["causal;window=512;dilation=2"]),
     "bigbird4k_b8_h12_d64": dict(B=8, H=12, T=4096, d=64, dtype="bf16",
                                  specs=["blocks;block=64;radius=1;random=3;seed=0;global=0:128"]),
+    "mistral32k_window4096_bwd": dict(kind="backward", B=1, H=32, T=32768, d=128, dtype="bf16",
+                                      specs=["causal;window=4096"]),
     "mistral_decode_b64_w4096": dict(kind="decode", B=64, H=32, Hkv=8, d=128, dtype="bf16",
                                      n_new=1, C=4096, pos_range=(4096, 32768),
                                      specs=["causal;window=4096"]),
@@ -114,6 +117,73 @@ def cpu_baseline(wl, specs, q, k, v, budget_s: float):
                   f"{dt:.1f} s fp64 on the host",
         "seconds": dt,
     }
+
+
+def backward_bench(args, wl):
+    """Backward pass: one step = one sparse_attn_bwd call (dQ, dK, dV) for a
+    forward computed once beforehand.  Algorithmic flops 8 d E: dV, dP, dQ and
+    dK each take 2 d per allowed cell (recomputing S is not counted)."""
+    import torch
+
+    from block_sparse_masked_spec_amd import binding as sa
+    from block_sparse_masked_spec_amd import inputs
+
+    B, H, T, d, spec = wl["B"], wl["H"], wl["T"], wl["d"], wl["specs"][0]
+    q, k, v = inputs.qkv(B, H, T, d, "bf16", args.seed)
+    g = inputs.qkv(B, H, T, d, "bf16", args.seed + 1)[0]
+    qd, kd, vd, gd = q.cuda(), k.cuda(), v.cuda(), g.cuda()
+    od = torch.empty_like(qd)
+    lse = torch.empty(B, H, T, dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(qd), torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+    sa.sparse_attn_fwd_lse(qd, kd, vd, od, lse, B, H, T, d, spec, stream)
+    E_total = sa.sparse_attn_count(spec, T) * B * H
+    flops = 8.0 * d * E_total
+
+    def step():
+        sa.sparse_attn_bwd(qd, kd, vd, od, gd, lse, dq, dk, dv, B, H, T, d, spec, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    secs = ms / 1e3
+    tf = flops / secs / 1e12
+    result = {
+        "metric": METRIC,
+        "value": E_total / secs,
+        "unit": "allowed cells/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid N(0,1) Q/K/V/dO, no dataset)",
+        "config": {"workload": args.workload, "B": B, "H": H, "T": T, "d": d, "mask_specs": [spec],
+                   "allowed_cells_per_step": E_total, "pass": "backward (dQ, dK, dV)",
+                   "parallelism": "single GPU"},
+        "effective_tflops": tf,
+        "wall_s_timed": wall,
+        "kernel_sha": kernel_sha(),
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / BF16_PEAK_TFLOPS, "traffic": load_traffic(args.workload),
+                     "kernel": "sa_bwd_dq_kernel + sa_bwd_dkv_kernel", "ms_per_launch": ms,
+                     "algorithmic_flops_per_step": flops},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
 
 
 def decode_bench(args, wl):
@@ -229,6 +299,8 @@ def main():
     wl = WORKLOADS[args.workload]
     if wl.get("kind") == "decode":
         return decode_bench(args, wl)
+    if wl.get("kind") == "backward":
+        return backward_bench(args, wl)
     B, H, T, d, dtype, specs = wl["B"], wl["H"], wl["T"], wl["d"], wl["dtype"], wl["specs"]
     fwd = sa.sparse_attn_fwd if dtype == "bf16" else sa.sparse_attn_fwd_f32
 
