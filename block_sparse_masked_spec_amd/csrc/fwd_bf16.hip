@@ -187,6 +187,18 @@ static __device__ __forceinline__ void issue(const Cursor& c, const FwdArgs& a, 
 }
 };
 
+// End of a tile: this wave's direct loads of the next tile have landed and
+// every wave has finished the current one.  Only vmcnt is drained (the
+// scalar plan reads already in flight for later tiles may stay in flight);
+// the scheduling barriers keep every LDS read of the current tile before
+// the barrier and every read of the next tile after it.
+__device__ __forceinline__ void tile_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt left alone
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int D, int NG, int NW>
 struct WaveState {
     using L = Lay<D, NW>;
@@ -373,15 +385,13 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
         cursor_advance(nxt, a);
         if (!nxt.done()) TileLoad<D, NW>::issue(nxt, a, Kp, Vp, kbuf1, vbuf1, wave, lane, T, ga0, gna, gb0, rs);
         run_tile(cur, kbuf0, vbuf0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        tile_barrier();
         if (nxt.done()) break;
         cur = nxt;
         cursor_advance(nxt, a);
         if (!nxt.done()) TileLoad<D, NW>::issue(nxt, a, Kp, Vp, kbuf0, vbuf0, wave, lane, T, ga0, gna, gb0, rs);
         run_tile(cur, kbuf1, vbuf1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        tile_barrier();
         cur = nxt;
     }
 
