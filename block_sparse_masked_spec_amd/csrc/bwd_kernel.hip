@@ -343,6 +343,338 @@ __global__ __launch_bounds__(kThreads) void sa_bwd_dkv_kernel(BwdArgs b) {
     }
 }
 
+// ------------------------------------------- bf16: tiles by direct loads
+// For bf16 (d = 64, 128) both kernels fill padded row-major LDS tiles with
+// direct global->LDS loads (16 bytes per lane, 1 KiB per instruction: the pad
+// chunk of each row loads a valid dummy), double-buffered so that the next
+// tile's loads run under the current tile's MFMAs.  The transposed operands
+// (K^T, Q^T, dO^T) are read from the same row-major tiles with transposing
+// LDS reads, so no transposed copy is staged.
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+typedef __attribute__((address_space(3))) s16x4* lptr_s16x4_t;
+__device__ __forceinline__ gptr_t as_global(const void* p) { return (gptr_t)p; }
+__device__ __forceinline__ lptr_t as_lds(void* p) { return (lptr_t)p; }
+__device__ __forceinline__ lptr_s16x4_t as_lds_s16x4(const void* p) { return (lptr_s16x4_t)(void*)p; }
+
+// End of a tile: this wave's direct loads have landed and every wave is done
+// with the current buffers; the scheduling barriers keep LDS reads on their
+// side of the barrier.
+__device__ __forceinline__ void dma_tile_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// This wave's share of the direct loads of one 64-row tile of two [T][d]
+// tensors into padded row-major LDS tiles.  row_of(r) is the source row of
+// tile row r (always a valid row).
+template <int D, typename RowOf>
+__device__ __forceinline__ void dma_rows2(__bf16* dst_a, __bf16* dst_b, const __bf16* src_a,
+                                          const __bf16* src_b, RowOf row_of, int wave, int lane) {
+    using S = Shape<__bf16, D>;
+    constexpr int CPR2 = S::CPR + 1;  // 16-byte chunks per padded row
+    constexpr int NINS = CPR2;        // 64 rows * CPR2 chunks / 64 lanes
+#pragma unroll
+    for (int ins = wave; ins < NINS; ins += kWaves) {
+        const int c = ins * 64 + lane;
+        const int row = c / CPR2, ch = c % CPR2;
+        const size_t off = size_t(row_of(row)) * D + (ch < S::CPR ? ch * 8 : 0);
+        __builtin_amdgcn_global_load_lds(as_global(src_a + off), as_lds(dst_a + ins * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(as_global(src_b + off), as_lds(dst_b + ins * 512), 16, 0, 0);
+    }
+}
+
+// acc[db] += rows(tile)^T . x with the transposed operand read from the
+// row-major tile: for lane l of 16-lane group g (i = l % 16), read 4 columns
+// starting at db*32 + (g%2)*16 + 4*(i%4) of tile row off + (l/32)*8 + i/4
+// (and 4 rows further); the hardware transposes within the group so that
+// lane l holds 8 consecutive rows of column db*32 + l%32.
+template <int D>
+__device__ __forceinline__ void tile_accumulate_tr(f32x16* acc, const __bf16* rows_lds,
+                                                   const f32x16* x, int lane) {
+    using S = Shape<__bf16, D>;
+    const int h = lane >> 5, i = lane & 15, g = (lane >> 4) & 1;
+    static_for<0, S::PKS>([&](auto kk_c) {
+        constexpr int kk = decltype(kk_c)::value;
+        constexpr int blk = (kk * 8) >> 4;
+        constexpr int rb = (kk * 8) & 15;
+        constexpr int off = blk * 32 + (rb >> 3) * 16;
+        const bf16x8 xf = Ops<__bf16>::template pack<rb>(x[blk]);
+#pragma unroll
+        for (int db = 0; db < S::NDB; ++db) {
+            const __bf16* p = rows_lds + (off + h * 8 + (i >> 2)) * S::KLD + db * 32 + g * 16 + 4 * (i & 3);
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(p));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(p + 4 * S::KLD));
+            const bf16x8 af =
+                __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, xf, acc[db], 0, 0, 0);
+        }
+    });
+}
+
+// Tiles of one query block of the forward plan: runs of in-place key tiles,
+// then gathered strided/global keys in chunks of 64.
+struct BwdCursor {
+    int run, run_end, kb, kb_end;
+    bool masked;
+    int gi, g_total;
+    __device__ bool inplace() const { return run < run_end; }
+    __device__ bool done() const { return !inplace() && gi >= g_total; }
+};
+
+__device__ __forceinline__ void bcur_enter(BwdCursor& c, const FwdArgs& a) {
+    if (c.run < c.run_end) {
+        c.kb = a.runs[2 * c.run];
+        const int w = a.runs[2 * c.run + 1];
+        c.kb_end = w & 0x7fffffff;
+        c.masked = w < 0;
+    }
+}
+
+__device__ __forceinline__ void bcur_advance(BwdCursor& c, const FwdArgs& a) {
+    if (c.inplace()) {
+        if (++c.kb >= c.kb_end) {
+            ++c.run;
+            bcur_enter(c, a);
+        }
+    } else {
+        c.gi += kBK;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void sa_bwd_dq_dma_kernel(BwdArgs b) {
+    using E = __bf16;
+    using S = Shape<E, D>;
+    using F = typename Ops<E>::frag;
+    const FwdArgs& a = b.f;
+    constexpr int TILE = kBK * S::KLD;
+    __shared__ __attribute__((aligned(1024))) E kbuf[2 * TILE];
+    __shared__ __attribute__((aligned(1024))) E vbuf[2 * TILE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, h = lane >> 5;
+    const int work = xcd_slice_index(blockIdx.x, gridDim.x);
+    const int n_qb = gridDim.x / a.BH;
+    const int bh = work / n_qb;
+    const int qb = a.qb_order[work % n_qb];
+    const int T = a.T;
+    const size_t base = size_t(bh) * size_t(T) * D;
+    const E* Qp = static_cast<const E*>(a.Q) + base;
+    const E* Kp = static_cast<const E*>(a.K) + base;
+    const E* Vp = static_cast<const E*>(a.V) + base;
+    const E* Op = static_cast<const E*>(a.O) + base;
+    const E* Gp = static_cast<const E*>(b.dO) + base;
+    const int qi = qb * kBQ + wave * 32 + n;
+
+    F qf[S::NKS], gf[S::NKS];
+    load_frags<E, D>(qf, Qp, qi, T, h);
+    load_frags<E, D>(gf, Gp, qi, T, h);
+    float Dq;
+    {
+        F of[S::NKS];
+        load_frags<E, D>(of, Op, qi, T, h);
+        const float part = frag_dot<E, D>(gf, of);
+        Dq = part + __shfl_xor(part, 32);
+    }
+    if (qi < T && h == 0) b.Dw[size_t(bh) * size_t(T) + size_t(qi)] = Dq;
+    const float lse2 = qi < T ? b.lse[size_t(bh) * size_t(T) + size_t(qi)] * kLog2e : 0.f;
+    const bool rowg = qi < T && ((a.rowbits[qi >> 5] >> (qi & 31)) & 1u);
+    const int qres = a.dil == 1 ? 0 : qi % a.dil;
+    const int qblk = a.blk > 0 ? min(qi, T - 1) / a.blk : 0;
+
+    f32x16 acc[S::NDB];
+#pragma unroll
+    for (int db = 0; db < S::NDB; ++db) acc[db] = f32x16{};
+
+    const int ga0 = a.gseg[4 * qb], ga1 = a.gseg[4 * qb + 1];
+    const int gb0 = a.gseg[4 * qb + 2], gb1 = a.gseg[4 * qb + 3];
+    const int gna = ga1 - ga0, gtot = gna + (gb1 - gb0);
+    auto gkey = [&](int slot) { return a.colkeys[slot < gna ? ga0 + slot : gb0 + (slot - gna)]; };
+
+    auto issue = [&](const BwdCursor& c, E* kd, E* vd) {
+        if (c.inplace()) {
+            const int k0 = c.kb * kBK;
+            dma_rows2<D>(kd, vd, Kp, Vp, [&](int r) { return min(k0 + r, T - 1); }, wave, lane);
+        } else {
+            const int g0 = c.gi;
+            dma_rows2<D>(kd, vd, Kp, Vp, [&](int r) { return gkey(min(g0 + r, gtot - 1)); }, wave, lane);
+        }
+    };
+    auto compute = [&](const BwdCursor& c, const E* kt, const E* vt) {
+        f32x16 s[2], dp[2];
+        tile_product<E, D>(s, kt, qf, n, h);
+        tile_product<E, D>(dp, vt, gf, n, h);
+        uint64_t aw = ~0ull;
+        if (c.inplace()) {
+            const int k0 = c.kb * kBK;
+            if (c.masked)
+                aw = allowed_word(a, qi, k0, rowg, a.colbits[k0 >> 6], qres,
+                                  a.dil == 1 ? 0 : k0 % a.dil, qblk);
+        } else {
+            aw = low_bits(gtot - c.gi);
+        }
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const bool ok = (aw >> reg_row(blk, r, h)) & 1;
+                const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[blk][r], a.scale_log2, -lse2)) : 0.f;
+                s[blk][r] = p * (dp[blk][r] - Dq);  // dS
+            }
+        tile_accumulate_tr<D>(acc, kt, s, lane);
+    };
+
+    // Tile t computes from slot t % 2 while tile t + 1 loads into the other.
+    BwdCursor cur{a.run_ptr[qb], a.run_ptr[qb + 1], 0, 0, false, 0, gtot};
+    bcur_enter(cur, a);
+    int slot = 0;
+    if (!cur.done()) issue(cur, kbuf, vbuf);
+    dma_tile_barrier();
+    while (!cur.done()) {
+        BwdCursor nxt = cur;
+        bcur_advance(nxt, a);
+        if (!nxt.done()) issue(nxt, kbuf + (slot ^ 1) * TILE, vbuf + (slot ^ 1) * TILE);
+        compute(cur, kbuf + slot * TILE, vbuf + slot * TILE);
+        dma_tile_barrier();
+        cur = nxt;
+        slot ^= 1;
+    }
+    if (qi < T) store_rows<E, D>(static_cast<E*>(b.dQ) + base, acc, qi, h, b.scale);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void sa_bwd_dkv_dma_kernel(BwdArgs b) {
+    using E = __bf16;
+    using S = Shape<E, D>;
+    using F = typename Ops<E>::frag;
+    const FwdArgs& a = b.f;
+    constexpr int TILE = kBQB * S::KLD;
+    __shared__ __attribute__((aligned(1024))) E qbuf[2 * TILE];
+    __shared__ __attribute__((aligned(1024))) E gbuf[2 * TILE];
+    __shared__ __attribute__((aligned(256))) float lbuf[2 * kBQB];
+    __shared__ __attribute__((aligned(256))) float dbuf[2 * kBQB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, h = lane >> 5;
+    const int work = xcd_slice_index(blockIdx.x, gridDim.x);
+    const int bh = work / b.n_kb;
+    const int kb = b.kb_order[work % b.n_kb];
+    const int T = a.T;
+    const size_t base = size_t(bh) * size_t(T) * D;
+    const E* Qp = static_cast<const E*>(a.Q) + base;
+    const E* Kp = static_cast<const E*>(a.K) + base;
+    const E* Vp = static_cast<const E*>(a.V) + base;
+    const E* Gp = static_cast<const E*>(b.dO) + base;
+    const float* Lp = b.lse + size_t(bh) * size_t(T);
+    const float* Dp = b.Dw + size_t(bh) * size_t(T);
+    const int kj = kb * kBKB + wave * 32 + n;
+
+    F kf[S::NKS], vf[S::NKS];
+    load_frags<E, D>(kf, Kp, kj, T, h);
+    load_frags<E, D>(vf, Vp, kj, T, h);
+    const bool colj = kj < T && ((a.colbits[kj >> 6] >> (kj & 63)) & 1);
+
+    f32x16 dk[S::NDB], dv[S::NDB];
+#pragma unroll
+    for (int db = 0; db < S::NDB; ++db) dk[db] = dv[db] = f32x16{};
+
+    // Query tiles of this key block: run r, tile qt.
+    int r = b.kb_ptr[kb];
+    const int r_end = b.kb_ptr[kb + 1];
+    int qt = 0, qt_end = 0;
+    bool masked = false;
+    auto enter = [&]() {
+        if (r < r_end) {
+            qt = b.kb_runs[2 * r];
+            const int w = b.kb_runs[2 * r + 1];
+            qt_end = w & 0x7fffffff;
+            masked = w < 0;
+        }
+    };
+    enter();
+    auto issue = [&](int q0, E* qd, E* gd, float* lsd, float* dsd) {
+        dma_rows2<D>(qd, gd, Qp, Gp, [&](int rr) { return min(q0 + rr, T - 1); }, wave, lane);
+        if (wave == 0) {
+            const int i = min(q0 + lane, T - 1);
+            __builtin_amdgcn_global_load_lds(as_global(Lp + i), as_lds(lsd), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(as_global(Dp + i), as_lds(dsd), 4, 0, 0);
+        }
+    };
+    auto compute = [&](int q0, bool msk, const E* qt_l, const E* gt_l, const float* ls, const float* dsv) {
+        f32x16 s[2], dp[2];
+        tile_product<E, D>(s, qt_l, kf, n, h);
+        tile_product<E, D>(dp, gt_l, vf, n, h);
+        uint64_t aw = ~0ull;
+        if (msk) {
+            uint64_t roww = 0;
+            const int w0 = q0 >> 5, nw = (T + 31) >> 5;
+            if (w0 < nw) roww = a.rowbits[w0];
+            if (w0 + 1 < nw) roww |= uint64_t(a.rowbits[w0 + 1]) << 32;
+            aw = kj < T ? allowed_word_T(a, kj, q0, colj, roww) : 0ull;
+        }
+        f32x16 p[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int r4 = 0; r4 < 16; r4 += 4) {
+                const int x0 = reg_row(blk, r4, h);
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + x0);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsv + x0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool ok = (aw >> (x0 + e)) & 1;
+                    const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[blk][r4 + e], a.scale_log2,
+                                                                      -l4[e] * kLog2e))
+                                        : 0.f;
+                    p[blk][r4 + e] = pv;
+                    s[blk][r4 + e] = pv * (dp[blk][r4 + e] - d4[e]);  // dS
+                }
+            }
+        tile_accumulate_tr<D>(dv, gt_l, p, lane);
+        tile_accumulate_tr<D>(dk, qt_l, s, lane);
+    };
+
+    // The (run, tile) sequence: tile t computes from slot t % 2 while tile
+    // t + 1 loads into the other.
+    bool have = r < r_end;
+    int cq = qt;
+    bool cm = masked;
+    auto step_next = [&]() {  // advance to the next tile; false when none
+        if (++qt >= qt_end) {
+            ++r;
+            if (r >= r_end) return false;
+            enter();
+        }
+        return true;
+    };
+    int slot = 0;
+    if (have) issue(cq * kBQB, qbuf, gbuf, lbuf, dbuf);
+    dma_tile_barrier();
+    while (have) {
+        const bool nh = step_next();
+        const int nq = qt;
+        const bool nm = masked;
+        const int o = slot ^ 1;
+        if (nh) issue(nq * kBQB, qbuf + o * TILE, gbuf + o * TILE, lbuf + o * kBQB, dbuf + o * kBQB);
+        compute(cq * kBQB, cm, qbuf + slot * TILE, gbuf + slot * TILE, lbuf + slot * kBQB,
+                dbuf + slot * kBQB);
+        dma_tile_barrier();
+        have = nh;
+        cq = nq;
+        cm = nm;
+        slot = o;
+    }
+    if (kj < T) {
+        store_rows<E, D>(static_cast<E*>(b.dK) + base, dk, kj, h, b.scale);
+        store_rows<E, D>(static_cast<E*>(b.dV) + base, dv, kj, h, 1.f);
+    }
+}
+
 template <typename E, int D>
 int launch_b(const BwdArgs& b, void* stream) {
     const unsigned g1 = static_cast<unsigned>(int64_t(b.f.BH) * ((b.f.T + kBQ - 1) / kBQ));
@@ -355,6 +687,18 @@ int launch_b(const BwdArgs& b, void* stream) {
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
+template <int D>
+int launch_b_dma(const BwdArgs& b, void* stream) {
+    const unsigned g1 = static_cast<unsigned>(int64_t(b.f.BH) * ((b.f.T + kBQ - 1) / kBQ));
+    hipLaunchKernelGGL((sa_bwd_dq_dma_kernel<D>), dim3(g1), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), b);
+    if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
+    const unsigned g2 = static_cast<unsigned>(int64_t(b.f.BH) * b.n_kb);
+    hipLaunchKernelGGL((sa_bwd_dkv_dma_kernel<D>), dim3(g2), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), b);
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
 }  // namespace
 
 int launch_bwd(int dtype, int d, const BwdArgs& b, void* stream) {
@@ -362,8 +706,8 @@ int launch_bwd(int dtype, int d, const BwdArgs& b, void* stream) {
         switch (d) {
             case 16: return launch_b<__bf16, 16>(b, stream);
             case 32: return launch_b<__bf16, 32>(b, stream);
-            case 64: return launch_b<__bf16, 64>(b, stream);
-            case 128: return launch_b<__bf16, 128>(b, stream);
+            case 64: return launch_b_dma<64>(b, stream);
+            case 128: return launch_b_dma<128>(b, stream);
         }
     } else if (dtype == SA_DTYPE_F32) {
         switch (d) {
