@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,9 +31,7 @@ METRIC = "allowed attention cells/s and effective TFLOP/s at 1 MI355X; % of bf16
 BF16_PEAK_TFLOPS = 2500.0
 F32_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_masked_spec_amd", "csrc", f)
-               for f in ("fwd_kernel.hip", "fwd_bf16.hip", "decode.hip", "bwd_kernel.hip",
-                         "mfma_tiles.hpp", "kernel_common.hpp", "internal.hpp")]
+CSRC = os.path.join(ROOT, "block_sparse_masked_spec_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = {
@@ -59,16 +58,42 @@ WORKLOADS = {
 DEFAULT_WORKLOAD = "mistral32k_window4096"
 
 
-def kernel_sha() -> str:
+def kernel_source(wl) -> str:
+    """The device source file of the kernels a workload times."""
+    kind = wl.get("kind", "forward")
+    if kind == "decode":
+        return "decode.hip"
+    if kind == "backward":
+        return "bwd_kernel.hip"
+    return "fwd_bf16.hip" if kernel_name(wl["dtype"], wl["d"]) == "sa_fwd_bf16_kernel" else "fwd_kernel.hip"
+
+
+def kernel_sha(wl) -> str:
+    """Hash of a workload's kernel source and the local headers it includes,
+    transitively: counter readings taken for other code do not carry over."""
     h = hashlib.sha256()
-    for f in KERNEL_SRCS:
-        h.update(open(f, "rb").read())
+    seen, todo = set(), [os.path.join(CSRC, kernel_source(wl))]
+    while todo:
+        f = os.path.normpath(todo.pop(0))
+        if f in seen:
+            continue
+        seen.add(f)
+        text = open(f, "rb").read()
+        h.update(os.path.basename(f).encode() + b"\0" + text)
+        for inc in re.findall(rb'^#include "([^"]+)"', text, re.M):
+            todo.append(os.path.join(os.path.dirname(f), inc.decode()))
     return h.hexdigest()[:16]
 
 
 def kernel_name(dtype: str, d: int) -> str:
     """The kernel that runs the forward for this dtype and head size."""
     return "sa_fwd_bf16_kernel" if dtype == "bf16" and d in (64, 128) else "sa_fwd_kernel"
+
+
+def bwd_kernel_names(dtype: str, d: int) -> str:
+    if dtype == "bf16" and d in (64, 128):
+        return "sa_bwd_dq_dma_kernel + sa_bwd_dkv_dma_kernel"
+    return "sa_bwd_dq_kernel + sa_bwd_dkv_kernel"
 
 
 def load_traffic(workload: str):
@@ -78,7 +103,7 @@ def load_traffic(workload: str):
     except (OSError, ValueError):
         return None
     entry = data.get(workload)
-    if not entry or entry.get("kernel_sha") != kernel_sha():
+    if not entry or entry.get("kernel_sha") != kernel_sha(WORKLOADS[workload]):
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -119,6 +144,24 @@ def cpu_baseline(wl, specs, q, k, v, budget_s: float):
     }
 
 
+def copy_calibration(args, result):
+    """With --copy-calibration-mib N, end the run with one device-to-device
+    copy of N MiB, so that a counter run can scale FETCH_SIZE / WRITE_SIZE
+    by what they read for a copy of known size."""
+    import torch
+
+    if args.copy_calibration_mib <= 0:
+        return
+    n = args.copy_calibration_mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    result["copy_calibration_bytes"] = {"read": n * 4, "write": n * 4}
+    del src, dst
+
+
 def backward_bench(args, wl):
     """Backward pass: one step = one sparse_attn_bwd call (dQ, dK, dV) for a
     forward computed once beforehand.  Algorithmic flops 8 d E: dV, dP, dQ and
@@ -139,6 +182,8 @@ def backward_bench(args, wl):
     sa.sparse_attn_fwd_lse(qd, kd, vd, od, lse, B, H, T, d, spec, stream)
     E_total = sa.sparse_attn_count(spec, T) * B * H
     flops = 8.0 * d * E_total
+    # Q, K, V, O, dO read once, dQ, dK, dV written once (bf16), LSE read.
+    alg_bytes = 8.0 * B * H * T * d * 2 + 4.0 * B * H * T
 
     def step():
         sa.sparse_attn_bwd(qd, kd, vd, od, gd, lse, dq, dk, dv, B, H, T, d, spec, stream)
@@ -175,13 +220,14 @@ def backward_bench(args, wl):
                    "parallelism": "single GPU"},
         "effective_tflops": tf,
         "wall_s_timed": wall,
-        "kernel_sha": kernel_sha(),
+        "kernel_sha": kernel_sha(wl),
         "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / BF16_PEAK_TFLOPS, "traffic": load_traffic(args.workload),
-                     "kernel": "sa_bwd_dq_kernel + sa_bwd_dkv_kernel", "ms_per_launch": ms,
-                     "algorithmic_flops_per_step": flops},
+                     "kernel": bwd_kernel_names(wl["dtype"], d), "ms_per_launch": ms,
+                     "algorithmic_flops_per_step": flops, "algorithmic_bytes_per_step": alg_bytes},
         "cpu_baseline": None,
     }
+    copy_calibration(args, result)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -248,21 +294,14 @@ def decode_bench(args, wl):
                    "parallelism": "single GPU"},
         "effective_tflops": flops / secs / 1e12,
         "wall_s_timed": wall,
-        "kernel_sha": kernel_sha(),
+        "kernel_sha": kernel_sha(wl),
         "roofline": {"bound": "hbm", "achieved": alg_bytes / secs / 1e9, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": alg_bytes / secs / 1e9 / HBM_PEAK_GBS,
                      "traffic": traffic, "kernel": "sa_decode_kernel", "ms_per_launch": ms,
                      "algorithmic_bytes_per_step": alg_bytes},
         "cpu_baseline": None,
     }
-    if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        result["copy_calibration_bytes"] = {"read": n * 4, "write": n * 4}
+    copy_calibration(args, result)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -378,19 +417,11 @@ def main():
         "effective_tflops": eff_tflops,
         "frac_bf16_peak": eff_tflops / BF16_PEAK_TFLOPS,
         "wall_s_timed": wall,
-        "kernel_sha": kernel_sha(),
+        "kernel_sha": kernel_sha(wl),
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        result["copy_calibration_bytes"] = {"read": n * 4, "write": n * 4}
-        del src, dst
+    copy_calibration(args, result)
     if args.cpu_budget > 0:
         q, k, v = host_sets[0]
         result["cpu_baseline"] = cpu_baseline(wl, specs, q, k, v, args.cpu_budget)

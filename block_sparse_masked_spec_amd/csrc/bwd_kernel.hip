@@ -369,46 +369,84 @@ __device__ __forceinline__ void dma_tile_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Tiles are 64 rows of D bf16 with no padding; the 16-byte chunk c of row r
+// sits at chunk position c ^ swz(r) of that row.  The XOR pattern (a linear
+// map of the row's low four bits) keeps both read patterns free of bank
+// conflicts: the 16-byte row reads of the first product (8 or 16 lanes on
+// distinct rows) and the 8-byte transposing reads (4 rows x 2 chunks per 16
+// lanes).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128)
+        return ((r & 1) ? 4 : 0) ^ ((r & 2) ? 10 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 3 : 0);
+    else
+        return ((r & 1) ? 2 : 0) ^ ((r & 2) ? 4 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 3 : 0);
+}
+
 // This wave's share of the direct loads of one 64-row tile of two [T][d]
-// tensors into padded row-major LDS tiles.  row_of(r) is the source row of
-// tile row r (always a valid row).
+// tensors: LDS chunk position p of row r receives source chunk p ^ swz(r).
+// row_of(r) is the source row of tile row r (always a valid row).
 template <int D, typename RowOf>
 __device__ __forceinline__ void dma_rows2(__bf16* dst_a, __bf16* dst_b, const __bf16* src_a,
                                           const __bf16* src_b, RowOf row_of, int wave, int lane) {
-    using S = Shape<__bf16, D>;
-    constexpr int CPR2 = S::CPR + 1;  // 16-byte chunks per padded row
-    constexpr int NINS = CPR2;        // 64 rows * CPR2 chunks / 64 lanes
+    constexpr int CPR = D / 8;       // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;    // rows per instruction
+    constexpr int NJ = CPR / kWaves; // instructions per wave
+    // Instruction j of this wave fills tile rows r0 + j * kWaves * RPI; the
+    // row's low four bits, hence its swizzle, do not depend on j.
+    const int r0 = wave * RPI + lane / CPR;
+    const int ch = (lane % CPR) ^ swz<D>(r0);
 #pragma unroll
-    for (int ins = wave; ins < NINS; ins += kWaves) {
-        const int c = ins * 64 + lane;
-        const int row = c / CPR2, ch = c % CPR2;
-        const size_t off = size_t(row_of(row)) * D + (ch < S::CPR ? ch * 8 : 0);
-        __builtin_amdgcn_global_load_lds(as_global(src_a + off), as_lds(dst_a + ins * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(as_global(src_b + off), as_lds(dst_b + ins * 512), 16, 0, 0);
+    for (int j = 0; j < NJ; ++j) {
+        const size_t off = size_t(row_of(r0 + j * kWaves * RPI)) * D + ch * 8;
+        const int lds = (wave + j * kWaves) * 512;
+        __builtin_amdgcn_global_load_lds(as_global(src_a + off), as_lds(dst_a + lds), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(as_global(src_b + off), as_lds(dst_b + lds), 16, 0, 0);
     }
 }
 
-// acc[db] += rows(tile)^T . x with the transposed operand read from the
-// row-major tile: for lane l of 16-lane group g (i = l % 16), read 4 columns
-// starting at db*32 + (g%2)*16 + 4*(i%4) of tile row off + (l/32)*8 + i/4
-// (and 4 rows further); the hardware transposes within the group so that
-// lane l holds 8 consecutive rows of column db*32 + l%32.
+// Product of rows blk*32 .. blk*32+31 of a swizzled 64-row tile with this
+// lane's fragments: out = rows . frag^T (rows are MFMA rows in the permuted
+// order, one column per lane).
 template <int D>
-__device__ __forceinline__ void tile_accumulate_tr(f32x16* acc, const __bf16* rows_lds,
-                                                   const f32x16* x, int lane) {
+__device__ __forceinline__ f32x16 half_product(const __bf16* tile, const bf16x8* f, int blk, int n,
+                                               int h) {
+    const int rr = swap23(n);
+    const int x = h ^ swz<D>(rr);  // chunk 2 ks + h lands at 2 ks ^ x
+    const __bf16* r = tile + (blk * 32 + rr) * D;
+    f32x16 out = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+        out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *reinterpret_cast<const bf16x8*>(r + ((2 * ks) ^ x) * 8), f[ks], out, 0, 0, 0);
+    return out;
+}
+
+// acc[db] += rows(blk half of the tile)^T . x, the transposed operand read
+// from the swizzled row-major tile: for lane l of 16-lane group g
+// (i = l % 16), read 4 columns starting at db*32 + (g%2)*16 + 4*(i%4) of
+// tile row off + (l/32)*8 + i/4 (and 4 rows further); the hardware
+// transposes within the group so that lane l holds 8 consecutive rows of
+// column db*32 + l%32.  x holds the half's 32 rows of this lane's column.
+template <int D>
+__device__ __forceinline__ void half_accumulate_tr(f32x16* acc, const __bf16* tile, const f32x16& x,
+                                                   int blk, int lane) {
     using S = Shape<__bf16, D>;
     const int h = lane >> 5, i = lane & 15, g = (lane >> 4) & 1;
-    static_for<0, S::PKS>([&](auto kk_c) {
-        constexpr int kk = decltype(kk_c)::value;
-        constexpr int blk = (kk * 8) >> 4;
-        constexpr int rb = (kk * 8) & 15;
-        constexpr int off = blk * 32 + (rb >> 3) * 16;
-        const bf16x8 xf = Ops<__bf16>::template pack<rb>(x[blk]);
+    const int r_lo = h * 8 + (i >> 2);                   // row within a 16-row group
+    const int cl = g * 2 + ((i & 3) >> 1);               // chunk within a 32-column block
+    const int half = (i & 1) * 4;                        // element offset in the chunk
+    const int y_lo = cl ^ swz<D>(r_lo), y_hi = cl ^ swz<D>(r_lo + 4);
+    static_for<0, 2>([&](auto rb_c) {
+        constexpr int rb = decltype(rb_c)::value * 8;
+        const int off = blk * 32 + (rb >> 3) * 16;
+        const bf16x8 xf = Ops<__bf16>::template pack<rb>(x);
 #pragma unroll
         for (int db = 0; db < S::NDB; ++db) {
-            const __bf16* p = rows_lds + (off + h * 8 + (i >> 2)) * S::KLD + db * 32 + g * 16 + 4 * (i & 3);
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(p));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(p + 4 * S::KLD));
+            const __bf16* p0 = tile + (off + r_lo) * D + ((db * 4) ^ y_lo) * 8 + half;
+            const __bf16* p1 = tile + (off + r_lo + 4) * D + ((db * 4) ^ y_hi) * 8 + half;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(p0));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(p1));
             const bf16x8 af =
                 __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, xf, acc[db], 0, 0, 0);
@@ -447,16 +485,17 @@ __device__ __forceinline__ void bcur_advance(BwdCursor& c, const FwdArgs& a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void sa_bwd_dq_dma_kernel(BwdArgs b) {
+__global__ __launch_bounds__(kThreads, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
     using E = __bf16;
     using S = Shape<E, D>;
     using F = typename Ops<E>::frag;
     const FwdArgs& a = b.f;
-    constexpr int TILE = kBK * S::KLD;
+    constexpr int TILE = kBK * D;
     __shared__ __attribute__((aligned(1024))) E kbuf[2 * TILE];
     __shared__ __attribute__((aligned(1024))) E vbuf[2 * TILE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, h = lane >> 5;
     const int work = xcd_slice_index(blockIdx.x, gridDim.x);
     const int n_qb = gridDim.x / a.BH;
@@ -506,9 +545,6 @@ __global__ __launch_bounds__(kThreads) void sa_bwd_dq_dma_kernel(BwdArgs b) {
         }
     };
     auto compute = [&](const BwdCursor& c, const E* kt, const E* vt) {
-        f32x16 s[2], dp[2];
-        tile_product<E, D>(s, kt, qf, n, h);
-        tile_product<E, D>(dp, vt, gf, n, h);
         uint64_t aw = ~0ull;
         if (c.inplace()) {
             const int k0 = c.kb * kBK;
@@ -518,15 +554,19 @@ __global__ __launch_bounds__(kThreads) void sa_bwd_dq_dma_kernel(BwdArgs b) {
         } else {
             aw = low_bits(gtot - c.gi);
         }
+        // One 32-key half at a time: S^T, dP^T, dS^T, then dQ^T += K^T dS^T.
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < 2; ++blk) {
+            f32x16 sv = half_product<D>(kt, qf, blk, n, h);
+            const f32x16 dp = half_product<D>(vt, gf, blk, n, h);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const bool ok = (aw >> reg_row(blk, r, h)) & 1;
-                const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[blk][r], a.scale_log2, -lse2)) : 0.f;
-                s[blk][r] = p * (dp[blk][r] - Dq);  // dS
+                const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sv[r], a.scale_log2, -lse2)) : 0.f;
+                sv[r] = p * (dp[r] - Dq);  // dS
             }
-        tile_accumulate_tr<D>(acc, kt, s, lane);
+            half_accumulate_tr<D>(acc, kt, sv, blk, lane);
+        }
     };
 
     // Tile t computes from slot t % 2 while tile t + 1 loads into the other.
@@ -548,18 +588,19 @@ __global__ __launch_bounds__(kThreads) void sa_bwd_dq_dma_kernel(BwdArgs b) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void sa_bwd_dkv_dma_kernel(BwdArgs b) {
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kernel(BwdArgs b) {
     using E = __bf16;
     using S = Shape<E, D>;
     using F = typename Ops<E>::frag;
     const FwdArgs& a = b.f;
-    constexpr int TILE = kBQB * S::KLD;
+    constexpr int TILE = kBQB * D;
     __shared__ __attribute__((aligned(1024))) E qbuf[2 * TILE];
     __shared__ __attribute__((aligned(1024))) E gbuf[2 * TILE];
     __shared__ __attribute__((aligned(256))) float lbuf[2 * kBQB];
     __shared__ __attribute__((aligned(256))) float dbuf[2 * kBQB];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, h = lane >> 5;
     const int work = xcd_slice_index(blockIdx.x, gridDim.x);
     const int bh = work / b.n_kb;
@@ -606,9 +647,6 @@ __global__ __launch_bounds__(kThreads) void sa_bwd_dkv_dma_kernel(BwdArgs b) {
         }
     };
     auto compute = [&](int q0, bool msk, const E* qt_l, const E* gt_l, const float* ls, const float* dsv) {
-        f32x16 s[2], dp[2];
-        tile_product<E, D>(s, qt_l, kf, n, h);
-        tile_product<E, D>(dp, gt_l, vf, n, h);
         uint64_t aw = ~0ull;
         if (msk) {
             uint64_t roww = 0;
@@ -617,9 +655,12 @@ __global__ __launch_bounds__(kThreads) void sa_bwd_dkv_dma_kernel(BwdArgs b) {
             if (w0 + 1 < nw) roww |= uint64_t(a.rowbits[w0 + 1]) << 32;
             aw = kj < T ? allowed_word_T(a, kj, q0, colj, roww) : 0ull;
         }
-        f32x16 p[2];
+        // One 32-query half at a time: S, dP, P and dS, then dV^T += dO^T P
+        // and dK^T += Q^T dS.
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < 2; ++blk) {
+            f32x16 sv = half_product<D>(qt_l, kf, blk, n, h);
+            f32x16 dp = half_product<D>(gt_l, vf, blk, n, h);
 #pragma unroll
             for (int r4 = 0; r4 < 16; r4 += 4) {
                 const int x0 = reg_row(blk, r4, h);
@@ -628,15 +669,15 @@ __global__ __launch_bounds__(kThreads) void sa_bwd_dkv_dma_kernel(BwdArgs b) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const bool ok = (aw >> (x0 + e)) & 1;
-                    const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[blk][r4 + e], a.scale_log2,
-                                                                      -l4[e] * kLog2e))
-                                        : 0.f;
-                    p[blk][r4 + e] = pv;
-                    s[blk][r4 + e] = pv * (dp[blk][r4 + e] - d4[e]);  // dS
+                    const float pv =
+                        ok ? __builtin_amdgcn_exp2f(fmaf(sv[r4 + e], a.scale_log2, -l4[e] * kLog2e)) : 0.f;
+                    sv[r4 + e] = pv;
+                    dp[r4 + e] = pv * (dp[r4 + e] - d4[e]);  // dS
                 }
             }
-        tile_accumulate_tr<D>(dv, gt_l, p, lane);
-        tile_accumulate_tr<D>(dk, qt_l, s, lane);
+            half_accumulate_tr<D>(dv, gt_l, sv, blk, lane);
+            half_accumulate_tr<D>(dk, qt_l, dp, blk, lane);
+        }
     };
 
     // The (run, tile) sequence: tile t computes from slot t % 2 while tile

@@ -227,6 +227,23 @@ struct WaveState {
                 for (int g = 0; g < NG; ++g)
                     s[g][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[g][ks], s[g][b], 0, 0, 0);
             }
+        // V^T fragment i (two transposed reads).  With one query group the
+        // whole tile's fragments are read here, so that they arrive while
+        // the softmax runs; with two there is no room and each is read just
+        // before its products.
+        auto vt_frag = [&](int i) {
+            const char* blk = vt + i * 1024 + lane * 8;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(blk));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(blk + 512));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        constexpr bool kEarlyV = NG == 1;
+        bf16x8 vfa[kEarlyV ? 4 * L::NDB : 1];
+        if constexpr (kEarlyV) {
+#pragma unroll
+            for (int i = 0; i < 4 * L::NDB; ++i) vfa[i] = vt_frag(i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         bf16x8 pf[NG][4];
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
@@ -279,17 +296,16 @@ struct WaveState {
                 }
             }
         }
-        // O^T += V^T P^T: one V^T fragment (two transposed reads) feeds every
-        // query group of the wave.
+        // O^T += V^T P^T: one V^T fragment feeds every query group of the wave.
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
             for (int db = 0; db < L::NDB; ++db) {
-                const char* blk = vt + (kk * L::NDB + db) * 1024 + lane * 8;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(blk));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(blk + 512));
-                const bf16x8 vf = __builtin_bit_cast(
-                    bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                bf16x8 vf;
+                if constexpr (kEarlyV)
+                    vf = vfa[kk * L::NDB + db];
+                else
+                    vf = vt_frag(kk * L::NDB + db);
 #pragma unroll
                 for (int g = 0; g < NG; ++g)
                     acc[g][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[g][kk], acc[g][db], 0, 0, 0);
