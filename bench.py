@@ -49,6 +49,8 @@ WORKLOADS = {
                                  specs=["blocks;block=64;radius=1;random=3;seed=0;global=0:128"]),
     "mistral32k_window4096_bwd": dict(kind="backward", B=1, H=32, T=32768, d=128, dtype="bf16",
                                       specs=["causal;window=4096"]),
+    "bigbird4k_b8_h12_d64_bwd": dict(kind="backward", B=8, H=12, T=4096, d=64, dtype="bf16",
+                                     specs=["blocks;block=64;radius=1;random=3;seed=0;global=0:128"]),
     "mistral_decode_b64_w4096": dict(kind="decode", B=64, H=32, Hkv=8, d=128, dtype="bf16",
                                      n_new=1, C=4096, pos_range=(4096, 32768),
                                      specs=["causal;window=4096"]),

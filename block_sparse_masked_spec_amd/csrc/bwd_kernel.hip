@@ -593,11 +593,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kern
     using S = Shape<E, D>;
     using F = typename Ops<E>::frag;
     const FwdArgs& a = b.f;
+    // Two slots as distinct objects, indexed statically (see the dQ kernel).
     constexpr int TILE = kBQB * D;
-    __shared__ __attribute__((aligned(1024))) E qbuf[2 * TILE];
-    __shared__ __attribute__((aligned(1024))) E gbuf[2 * TILE];
-    __shared__ __attribute__((aligned(256))) float lbuf[2 * kBQB];
-    __shared__ __attribute__((aligned(256))) float dbuf[2 * kBQB];
+    __shared__ __attribute__((aligned(1024))) E qbuf0[TILE];
+    __shared__ __attribute__((aligned(1024))) E gbuf0[TILE];
+    __shared__ __attribute__((aligned(1024))) E qbuf1[TILE];
+    __shared__ __attribute__((aligned(1024))) E gbuf1[TILE];
+    __shared__ __attribute__((aligned(256))) float lbuf0[kBQB], dbuf0[kBQB], lbuf1[kBQB], dbuf1[kBQB];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -693,22 +695,51 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kern
         }
         return true;
     };
-    int slot = 0;
-    if (have) issue(cq * kBQB, qbuf, gbuf, lbuf, dbuf);
+    if (have) issue(cq * kBQB, qbuf0, gbuf0, lbuf0, dbuf0);
     dma_tile_barrier();
-    while (have) {
-        const bool nh = step_next();
-        const int nq = qt;
-        const bool nm = masked;
-        const int o = slot ^ 1;
-        if (nh) issue(nq * kBQB, qbuf + o * TILE, gbuf + o * TILE, lbuf + o * kBQB, dbuf + o * kBQB);
-        compute(cq * kBQB, cm, qbuf + slot * TILE, gbuf + slot * TILE, lbuf + slot * kBQB,
-                dbuf + slot * kBQB);
+    if constexpr (D == 64) {
+        // Two waves per SIMD leave no registers for a second copy of the
+        // loop body: the slot is chosen at run time (each tile's reads then
+        // wait for the next tile's loads, which the other wave covers).
+        int slot = 0;
+        while (have) {
+            const bool nh = step_next();
+            const int nq = qt;
+            const bool nm = masked;
+            if (nh) {
+                if (slot)
+                    issue(nq * kBQB, qbuf0, gbuf0, lbuf0, dbuf0);
+                else
+                    issue(nq * kBQB, qbuf1, gbuf1, lbuf1, dbuf1);
+            }
+            compute(cq * kBQB, cm, slot ? qbuf1 : qbuf0, slot ? gbuf1 : gbuf0, slot ? lbuf1 : lbuf0,
+                    slot ? dbuf1 : dbuf0);
+            dma_tile_barrier();
+            have = nh;
+            cq = nq;
+            cm = nm;
+            slot ^= 1;
+        }
+    }
+    while (D != 64 && have) {
+        bool nh = step_next();
+        int nq = qt;
+        bool nm = masked;
+        if (nh) issue(nq * kBQB, qbuf1, gbuf1, lbuf1, dbuf1);
+        compute(cq * kBQB, cm, qbuf0, gbuf0, lbuf0, dbuf0);
+        dma_tile_barrier();
+        if (!nh) break;
+        cq = nq;
+        cm = nm;
+        nh = step_next();
+        nq = qt;
+        nm = masked;
+        if (nh) issue(nq * kBQB, qbuf0, gbuf0, lbuf0, dbuf0);
+        compute(cq * kBQB, cm, qbuf1, gbuf1, lbuf1, dbuf1);
         dma_tile_barrier();
         have = nh;
         cq = nq;
         cm = nm;
-        slot = o;
     }
     if (kj < T) {
         store_rows<E, D>(static_cast<E*>(b.dK) + base, dk, kj, h, b.scale);
