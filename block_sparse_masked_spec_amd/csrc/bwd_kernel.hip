@@ -408,17 +408,26 @@ __device__ __forceinline__ void dma_rows2(__bf16* dst_a, __bf16* dst_b, const __
 // Product of rows blk*32 .. blk*32+31 of a swizzled 64-row tile with this
 // lane's fragments: out = rows . frag^T (rows are MFMA rows in the permuted
 // order, one column per lane).
-template <int D>
+template <int D, bool PRE = false>
 __device__ __forceinline__ f32x16 half_product(const __bf16* tile, const bf16x8* f, int blk, int n,
                                                int h) {
     const int rr = swap23(n);
     const int x = h ^ swz<D>(rr);  // chunk 2 ks + h lands at 2 ks ^ x
     const __bf16* r = tile + (blk * 32 + rr) * D;
     f32x16 out = f32x16{};
+    if constexpr (PRE) {
+        bf16x8 a[D / 16];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-        out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(r + ((2 * ks) ^ x) * 8), f[ks], out, 0, 0, 0);
+        for (int ks = 0; ks < D / 16; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(r + ((2 * ks) ^ x) * 8);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], f[ks], out, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                *reinterpret_cast<const bf16x8*>(r + ((2 * ks) ^ x) * 8), f[ks], out, 0, 0, 0);
+    }
     return out;
 }
 
@@ -428,7 +437,7 @@ __device__ __forceinline__ f32x16 half_product(const __bf16* tile, const bf16x8*
 // tile row off + (l/32)*8 + i/4 (and 4 rows further); the hardware
 // transposes within the group so that lane l holds 8 consecutive rows of
 // column db*32 + l%32.  x holds the half's 32 rows of this lane's column.
-template <int D>
+template <int D, bool PRE = false>
 __device__ __forceinline__ void half_accumulate_tr(f32x16* acc, const __bf16* tile, const f32x16& x,
                                                    int blk, int lane) {
     using S = Shape<__bf16, D>;
@@ -437,21 +446,44 @@ __device__ __forceinline__ void half_accumulate_tr(f32x16* acc, const __bf16* ti
     const int cl = g * 2 + ((i & 3) >> 1);               // chunk within a 32-column block
     const int half = (i & 1) * 4;                        // element offset in the chunk
     const int y_lo = cl ^ swz<D>(r_lo), y_hi = cl ^ swz<D>(r_lo + 4);
-    static_for<0, 2>([&](auto rb_c) {
-        constexpr int rb = decltype(rb_c)::value * 8;
-        const int off = blk * 32 + (rb >> 3) * 16;
-        const bf16x8 xf = Ops<__bf16>::template pack<rb>(x);
+    if constexpr (PRE) {
+        bf16x8 af[2][S::NDB];
 #pragma unroll
-        for (int db = 0; db < S::NDB; ++db) {
-            const __bf16* p0 = tile + (off + r_lo) * D + ((db * 4) ^ y_lo) * 8 + half;
-            const __bf16* p1 = tile + (off + r_lo + 4) * D + ((db * 4) ^ y_hi) * 8 + half;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(p0));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(p1));
-            const bf16x8 af =
-                __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, xf, acc[db], 0, 0, 0);
-        }
-    });
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int db = 0; db < S::NDB; ++db) {
+                const int off = blk * 32 + q * 16;
+                const __bf16* p0 = tile + (off + r_lo) * D + ((db * 4) ^ y_lo) * 8 + half;
+                const __bf16* p1 = tile + (off + r_lo + 4) * D + ((db * 4) ^ y_hi) * 8 + half;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(p0));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(p1));
+                af[q][db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, 2>([&](auto rb_c) {
+            constexpr int rb = decltype(rb_c)::value * 8;
+            const bf16x8 xf = Ops<__bf16>::template pack<rb>(x);
+#pragma unroll
+            for (int db = 0; db < S::NDB; ++db)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb >> 3][db], xf, acc[db], 0, 0, 0);
+        });
+    } else {
+        static_for<0, 2>([&](auto rb_c) {
+            constexpr int rb = decltype(rb_c)::value * 8;
+            const int off = blk * 32 + (rb >> 3) * 16;
+            const bf16x8 xf = Ops<__bf16>::template pack<rb>(x);
+    #pragma unroll
+            for (int db = 0; db < S::NDB; ++db) {
+                const __bf16* p0 = tile + (off + r_lo) * D + ((db * 4) ^ y_lo) * 8 + half;
+                const __bf16* p1 = tile + (off + r_lo + 4) * D + ((db * 4) ^ y_hi) * 8 + half;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(p0));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(p1));
+                const bf16x8 af =
+                    __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, xf, acc[db], 0, 0, 0);
+            }
+        });
+    }
 }
 
 // Tiles of one query block of the forward plan: runs of in-place key tiles,
@@ -661,8 +693,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kern
         // and dK^T += Q^T dS.
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            f32x16 sv = half_product<D>(qt_l, kf, blk, n, h);
-            f32x16 dp = half_product<D>(gt_l, vf, blk, n, h);
+            f32x16 sv = half_product<D, D == 128>(qt_l, kf, blk, n, h);
+            f32x16 dp = half_product<D, D == 128>(gt_l, vf, blk, n, h);
 #pragma unroll
             for (int r4 = 0; r4 < 16; r4 += 4) {
                 const int x0 = reg_row(blk, r4, h);
@@ -677,8 +709,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kern
                     dp[r4 + e] = pv * (dp[r4 + e] - d4[e]);  // dS
                 }
             }
-            half_accumulate_tr<D>(dv, gt_l, sv, blk, lane);
-            half_accumulate_tr<D>(dk, qt_l, dp, blk, lane);
+            half_accumulate_tr<D, D == 128>(dv, gt_l, sv, blk, lane);
+            half_accumulate_tr<D, D == 128>(dk, qt_l, dp, blk, lane);
         }
     };
 
