@@ -42,12 +42,12 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 class PlanCache {
   public:
-    // Returns SA_OK and a device plan for (spec, T) on the current device.
-    int get(const sa_mask& m, int T, DevicePlan* out) {
+    // Returns SA_OK and a device plan for (spec, T, bq) on the current device.
+    int get(const sa_mask& m, int T, int bq, DevicePlan* out) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return SA_ERR_HIP;
         std::string key = sa::canonical_spec(m) + "|T=" + std::to_string(T) + "|bq=" +
-                          std::to_string(sa::kBQ) + "|bk=" + std::to_string(sa::kBK) +
+                          std::to_string(bq) + "|bk=" + std::to_string(sa::kBK) +
                           "|dev=" + std::to_string(dev);
         std::lock_guard<std::mutex> lock(mu_);
         auto it = plans_.find(key);
@@ -55,7 +55,7 @@ class PlanCache {
             *out = it->second.plan;
             return SA_OK;
         }
-        HostPlan hp = sa::build_plan(MaskRule(m, T), sa::kBQ, sa::kBK);
+        HostPlan hp = sa::build_plan(MaskRule(m, T), bq, sa::kBK);
         DevicePlan dp;
         dp.n_qb = hp.n_qb;
         size_t off = 0;
@@ -268,9 +268,10 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     const int sub = sa::residue_split(m, T, d, dtype) ? m.dilation : 1;
     if (sub > 1) m.dilation = 1;
     const int Ts = T / sub;
-    if (BH * sub * ((int64_t(Ts) + sa::kBQ - 1) / sa::kBQ) > INT32_MAX) return SA_ERR_SHAPE;
+    const int bq = sa::fwd_query_block(m, d, dtype);
+    if (BH * sub * ((int64_t(Ts) + bq - 1) / bq) > INT32_MAX) return SA_ERR_SHAPE;
     DevicePlan dp;
-    rc = cache().get(m, Ts, &dp);
+    rc = cache().get(m, Ts, bq, &dp);
     if (rc != SA_OK) return rc;
     sa::FwdArgs a;
     a.Q = Q;
@@ -300,6 +301,7 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     a.blk_ptr = reinterpret_cast<const int32_t*>(base + dp.off_blk_ptr);
     a.blk_iv = reinterpret_cast<const int32_t*>(base + dp.off_blk_iv);
     a.lse = lse;
+    a.bq = bq;
     const int64_t grid = int64_t(a.BH) * dp.n_qb;
     int lrc = sa::launch_fwd_fast(dtype, d, a, grid, stream);
     if (lrc == SA_ERR_UNSUPPORTED && sub == 1) lrc = sa::launch_fwd(dtype, d, a, grid, stream);
@@ -337,7 +339,7 @@ int backward(int dtype, const void* Q, const void* K, const void* V, const void*
     int rc = parse_for(spec, T, &m);
     if (rc != SA_OK) return rc;
     DevicePlan dp;
-    rc = cache().get(m, T, &dp);
+    rc = cache().get(m, T, sa::kBQ, &dp);
     if (rc != SA_OK) return rc;
     sa::BwdDevicePlan bp;
     rc = cache().get_bwd(m, T, &bp);
@@ -374,6 +376,7 @@ int backward(int dtype, const void* Q, const void* K, const void* V, const void*
     a.blk_ptr = reinterpret_cast<const int32_t*>(base + dp.off_blk_ptr);
     a.blk_iv = reinterpret_cast<const int32_t*>(base + dp.off_blk_iv);
     a.lse = nullptr;
+    a.bq = sa::kBQ;
     b.dO = dO;
     b.lse = lse;
     b.dQ = dQ;
@@ -580,6 +583,7 @@ SA_EXPORT int sparse_attn_plan_info(const char* mask_spec, int T, int d, int dty
         sa_mask mp = m;
         if (sub > 1) mp.dilation = 1;
         MaskRule prule(mp, T / sub);
+        bq = sa::fwd_query_block(mp, d, dtype);
         HostPlan hp = sa::build_plan(prule, bq, bk);
         std::memset(info, 0, sizeof(*info));
         info->bq = bq;

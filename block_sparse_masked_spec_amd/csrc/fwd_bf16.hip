@@ -322,7 +322,8 @@ struct Occupancy {
 
 template <int D, int NG, int NW, bool SUB>
 __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_bf16_kernel(FwdArgs a) {
-    static_assert(kBQ == NW * NG * 32, "waves x groups x 32 queries = one query block");
+    constexpr int BQ = NW * NG * 32;  // waves x groups x 32 queries = one query block
+    static_assert(BQ == kBQ || BQ == 64, "query blocks of the plans: 128 or 64 rows");
     using L = Lay<D, NW>;
     // Two buffers as distinct objects, indexed statically (the loop below is
     // unrolled by two), so the compiler can tell the prefetch into one from
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
     const __bf16* Kp = static_cast<const __bf16*>(a.K) + base;
     const __bf16* Vp = static_cast<const __bf16*>(a.V) + base;
     __bf16* Op = static_cast<__bf16*>(a.O) + base;
-    const int q_base = qb * kBQ + wave * NG * 32;
+    const int q_base = qb * BQ + wave * NG * 32;
 
     WaveState<D, NG, NW> st;
     bool rowg[NG];
@@ -463,11 +464,13 @@ int fast_variant() {
 int launch_fwd_fast(int dtype, int d, const FwdArgs& a, int64_t grid, void* stream) {
     if (dtype != SA_DTYPE_BF16) return SA_ERR_UNSUPPORTED;
     const bool wide = fast_variant() == 1;
+    if (a.sub > 1 && a.bq != kBQ) return SA_ERR_UNSUPPORTED;
     if (a.sub > 1) {  // interleaved subsequences: strided rows
         if (d == 128) return launch_t<128, 1, 4, true>(a, grid, stream);
         if (d == 64) return launch_t<64, 1, 4, true>(a, grid, stream);
         return SA_ERR_UNSUPPORTED;
     }
+    if (a.bq == 64) return d == 64 ? launch_t<64, 1, 2>(a, grid, stream) : SA_ERR_UNSUPPORTED;
     if (d == 128) return wide ? launch_t<128, 2, 2>(a, grid, stream) : launch_t<128, 1, 4>(a, grid, stream);
     if (d == 64) return wide ? launch_t<64, 2, 2>(a, grid, stream) : launch_t<64, 1, 4>(a, grid, stream);
     return SA_ERR_UNSUPPORTED;

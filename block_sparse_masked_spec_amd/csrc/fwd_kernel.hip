@@ -231,6 +231,7 @@ int launch_t(const FwdArgs& a, int64_t grid, void* stream) {
 
 int launch_fwd(int dtype, int d, const FwdArgs& a, int64_t grid, void* stream) {
     if (grid < 1) return SA_ERR_SHAPE;
+    if (a.bq != kBQ) return SA_ERR_UNSUPPORTED;  // 128-row query blocks only
     if (dtype == SA_DTYPE_BF16) {
         switch (d) {
             case 16: return launch_t<__bf16, 16>(a, grid, stream);

@@ -157,6 +157,7 @@ struct FwdArgs {
     const uint64_t* colbits;
     const uint32_t* rowbits;
     float* lse;  // optional [BH][T] output: natural-log sum of exp of the row's scores
+    int32_t bq;  // query rows per tile of the plan (kBQ, or 64: fast path only)
 };
 
 constexpr int kBQ = 128;
@@ -221,6 +222,16 @@ int launch_decode(int d, const DecodeArgs& args, void* stream);
 inline bool residue_split(const sa_mask& m, int T, int d, int dtype) {
     return m.dilation > 1 && m.stride == 0 && m.n_global == 0 && T % m.dilation == 0 &&
            dtype == SA_DTYPE_BF16 && (d == 64 || d == 128);
+}
+
+// Query rows per tile of the forward plan.  Block mode with 64-key blocks
+// runs 64-query tiles on the bf16 d = 64 fast path: every tile then lies in
+// one query block, whose key blocks (neighbours, random picks, globals) are
+// whole tiles, instead of mixing two query blocks' random sets.
+inline int fwd_query_block(const sa_mask& m, int d, int dtype) {
+    return (m.block > 0 && m.block % 128 != 0 && m.block % 64 == 0 && dtype == SA_DTYPE_BF16 && d == 64)
+               ? 64
+               : kBQ;
 }
 
 // Launch the fused forward kernel; returns SA_OK or SA_ERR_HIP.

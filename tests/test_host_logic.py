@@ -259,6 +259,22 @@ def test_plan_info_of_dilated_windows():
     assert sa.sparse_attn_plan_info(spec, T, 32)["subsequences"] == 1
 
 
+
+def test_plan_info_of_64_key_blocks():
+    """Block mode with 64-key blocks runs 64-query tiles on the bf16 d = 64
+    path: each tile lies in one query block, so with no strided keys the
+    executed cells equal the allowed cells.  Other shapes keep 128 rows."""
+    spec, T = "blocks;block=64;radius=1;random=3;seed=0;global=0:128", 4096
+    info = sa.sparse_attn_plan_info(spec, T, 64)
+    assert (info["bq"], info["bk"], info["n_qb"]) == (64, 64, 64)
+    assert info["allowed_cells"] == oracle.count(spec, T)
+    assert info["executed_cells"] == info["allowed_cells"]
+    for d, dtype in [(128, sa.SA_DTYPE_BF16), (64, sa.SA_DTYPE_F32), (32, sa.SA_DTYPE_BF16)]:
+        assert sa.sparse_attn_plan_info(spec, T, d, dtype)["bq"] == 128
+    for other in ["blocks;block=128;radius=1;random=2;seed=0", "blocks;block=32;random=2;seed=1",
+                  "causal;window=256"]:
+        assert sa.sparse_attn_plan_info(other, T, 64)["bq"] == 128
+
 def test_count_and_map_errors():
     lib = sa.load()
     v = ctypes.c_int64(0)
