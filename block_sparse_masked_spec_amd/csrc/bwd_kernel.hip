@@ -498,8 +498,8 @@ struct BwdCursor {
 
 __device__ __forceinline__ void bcur_enter(BwdCursor& c, const FwdArgs& a) {
     if (c.run < c.run_end) {
-        c.kb = a.runs[2 * c.run];
-        const int w = a.runs[2 * c.run + 1];
+        c.kb = ldc(a.runs, 2 * c.run);
+        const int w = ldc(a.runs, 2 * c.run + 1);
         c.kb_end = w & 0x7fffffff;
         c.masked = w < 0;
     }
@@ -532,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
     const int work = xcd_slice_index(blockIdx.x, gridDim.x);
     const int n_qb = gridDim.x / a.BH;
     const int bh = work / n_qb;
-    const int qb = a.qb_order[work % n_qb];
+    const int qb = ldc(a.qb_order, work % n_qb);
     const int T = a.T;
     const size_t base = size_t(bh) * size_t(T) * D;
     const E* Qp = static_cast<const E*>(a.Q) + base;
@@ -562,8 +562,8 @@ __global__ __launch_bounds__(kThreads, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
 #pragma unroll
     for (int db = 0; db < S::NDB; ++db) acc[db] = f32x16{};
 
-    const int ga0 = a.gseg[4 * qb], ga1 = a.gseg[4 * qb + 1];
-    const int gb0 = a.gseg[4 * qb + 2], gb1 = a.gseg[4 * qb + 3];
+    const int ga0 = ldc(a.gseg, 4 * qb), ga1 = ldc(a.gseg, 4 * qb + 1);
+    const int gb0 = ldc(a.gseg, 4 * qb + 2), gb1 = ldc(a.gseg, 4 * qb + 3);
     const int gna = ga1 - ga0, gtot = gna + (gb1 - gb0);
     auto gkey = [&](int slot) { return a.colkeys[slot < gna ? ga0 + slot : gb0 + (slot - gna)]; };
 
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(kThreads, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
         if (c.inplace()) {
             const int k0 = c.kb * kBK;
             if (c.masked)
-                aw = allowed_word(a, qi, k0, rowg, a.colbits[k0 >> 6], qres,
+                aw = allowed_word(a, qi, k0, rowg, ldc(a.colbits, k0 >> 6), qres,
                                   a.dil == 1 ? 0 : k0 % a.dil, qblk);
         } else {
             aw = low_bits(gtot - c.gi);
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(kThreads, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
     };
 
     // Tile t computes from slot t % 2 while tile t + 1 loads into the other.
-    BwdCursor cur{a.run_ptr[qb], a.run_ptr[qb + 1], 0, 0, false, 0, gtot};
+    BwdCursor cur{ldc(a.run_ptr, qb), ldc(a.run_ptr, qb + 1), 0, 0, false, 0, gtot};
     bcur_enter(cur, a);
     int slot = 0;
     if (!cur.done()) issue(cur, kbuf, vbuf);
@@ -638,7 +638,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kern
     const int n = lane & 31, h = lane >> 5;
     const int work = xcd_slice_index(blockIdx.x, gridDim.x);
     const int bh = work / b.n_kb;
-    const int kb = b.kb_order[work % b.n_kb];
+    const int kb = ldc(b.kb_order, work % b.n_kb);
     const int T = a.T;
     const size_t base = size_t(bh) * size_t(T) * D;
     const E* Qp = static_cast<const E*>(a.Q) + base;
@@ -659,14 +659,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kern
     for (int db = 0; db < S::NDB; ++db) dk[db] = dv[db] = f32x16{};
 
     // Query tiles of this key block: run r, tile qt.
-    int r = b.kb_ptr[kb];
-    const int r_end = b.kb_ptr[kb + 1];
+    int r = ldc(b.kb_ptr, kb);
+    const int r_end = ldc(b.kb_ptr, kb + 1);
     int qt = 0, qt_end = 0;
     bool masked = false;
     auto enter = [&]() {
         if (r < r_end) {
-            qt = b.kb_runs[2 * r];
-            const int w = b.kb_runs[2 * r + 1];
+            qt = ldc(b.kb_runs, 2 * r);
+            const int w = ldc(b.kb_runs, 2 * r + 1);
             qt_end = w & 0x7fffffff;
             masked = w < 0;
         }
@@ -685,8 +685,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kern
         if (msk) {
             uint64_t roww = 0;
             const int w0 = q0 >> 5, nw = (T + 31) >> 5;
-            if (w0 < nw) roww = a.rowbits[w0];
-            if (w0 + 1 < nw) roww |= uint64_t(a.rowbits[w0 + 1]) << 32;
+            if (w0 < nw) roww = ldc(a.rowbits, w0);
+            if (w0 + 1 < nw) roww |= uint64_t(ldc(a.rowbits, w0 + 1)) << 32;
             aw = kj < T ? allowed_word_T(a, kj, q0, colj, roww) : 0ull;
         }
         // One 32-query half at a time: S, dP, P and dS, then dV^T += dO^T P

@@ -50,14 +50,6 @@ __device__ __forceinline__ gptr_t as_global(const void* p) { return (gptr_t)p; }
 __device__ __forceinline__ lptr_t as_lds(void* p) { return (lptr_t)p; }
 __device__ __forceinline__ lptr_s16x4_t as_lds_s16x4(const void* p) { return (lptr_s16x4_t)(void*)p; }
 
-// The plan is written before the launch and only read by the kernel, so it
-// can be read through the constant address space: uniform reads become
-// scalar loads, which do not share a wait counter with the tile loads.
-template <typename T>
-__device__ __forceinline__ T ldc(const T* p, int i) {
-    return ((const __attribute__((address_space(4))) T*)p)[i];
-}
-
 constexpr float kLazyTau = 8.0f;  // log2-domain slack before the max moves
 static_assert(kBK == 64, "one column-bit word per key tile");
 

@@ -1,4 +1,4 @@
-// Device helpers shared by the forward kernels.
+// Device helpers shared by the forward and backward kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -9,6 +9,14 @@
 namespace sa {
 
 constexpr int kXcds = 8;  // MI355X: 8 accelerator dies, each with its own L2
+
+// The plan is written before the launch and only read by the kernel, so it
+// can be read through the constant address space: uniform reads become
+// scalar loads, which do not share a wait counter with the tile loads.
+template <typename T>
+__device__ __forceinline__ T ldc(const T* p, int i) {
+    return ((const __attribute__((address_space(4))) T*)p)[i];
+}
 
 // Workgroups are handed to the dies round-robin (block b runs on die b % 8).
 // Remap block ids so that each die walks one contiguous slice of the work
