@@ -9,7 +9,8 @@
 //   dK_j = sum_i ds_ij q_i / sqrt(d),  dV_j = sum_i p_ij dO_i.
 // Only allowed pairs are visited, tile by tile, as in the forward.
 //
-// Two kernels, no atomics:
+// Two kernels, no atomics (sa_bwd_dq_kernel / sa_bwd_dkv_kernel for fp32 and
+// small d; the _dma pair further down for bf16 d = 64, 128, same work):
 //   * sa_bwd_dq_kernel: one workgroup per (head, 128-query block), walking
 //     the forward plan (in-place key tiles, then gathered strided/global
 //     keys).  Per 64-key tile: S^T = K Q^T and dP^T = V dO^T on MFMA (keys
@@ -344,12 +345,13 @@ __global__ __launch_bounds__(kThreads) void sa_bwd_dkv_kernel(BwdArgs b) {
 }
 
 // ------------------------------------------- bf16: tiles by direct loads
-// For bf16 (d = 64, 128) both kernels fill padded row-major LDS tiles with
-// direct global->LDS loads (16 bytes per lane, 1 KiB per instruction: the pad
-// chunk of each row loads a valid dummy), double-buffered so that the next
-// tile's loads run under the current tile's MFMAs.  The transposed operands
-// (K^T, Q^T, dO^T) are read from the same row-major tiles with transposing
-// LDS reads, so no transposed copy is staged.
+// For bf16 (d = 64, 128) the two kernels below (sa_bwd_dq_dma_kernel,
+// sa_bwd_dkv_dma_kernel) fill unpadded, XOR-swizzled row-major LDS tiles
+// with direct global->LDS loads (16 bytes per lane, 1 KiB per instruction),
+// double-buffered so that the next tile's loads run under the current
+// tile's MFMAs.  The transposed operands (K^T, Q^T, dO^T) are read from the
+// same row-major tiles with transposing LDS reads, so no transposed copy is
+// staged.  Each 64-row tile is processed as two 32-row halves.
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(1))) void* gptr_t;
