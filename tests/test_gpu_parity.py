@@ -131,6 +131,19 @@ def test_dilated_interleaved_lengths(gpu, T, d):
         full_check(gpu, spec, 1, 3, T, d, "bf16", seed=T + d)
 
 
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 130, 300])
+def test_block_mode_64_row_tiles_lengths(gpu, T):
+    """Block mode with 64-key blocks at bf16 d = 64 runs 64-query tiles;
+    lengths cover one partial tile, exact tiles and ragged tails, with and
+    without strided and global keys."""
+    specs = ["blocks;block=64;radius=1;random=2;seed=4"]
+    if T >= 3:
+        specs.append("blocks;block=64;random=3;seed=1;stride=29;global=0:3")
+    for spec in specs:
+        assert gpu.sparse_attn_plan_info(spec, T, 64)["bq"] == 64
+        full_check(gpu, spec, 2, 2, T, 64, "bf16", seed=T)
+
 def test_window_one_returns_values_exactly(gpu):
     q, k, v = inputs.qkv(2, 3, 200, 64, "bf16", 5)
     got = run_gpu(gpu, "causal;window=1", q, k, v)
