@@ -691,12 +691,18 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kern
             if (w0 + 1 < nw) roww |= uint64_t(ldc(a.rowbits, w0 + 1)) << 32;
             aw = kj < T ? allowed_word_T(a, kj, q0, colj, roww) : 0ull;
         }
-        // One 32-query half at a time: S, dP, P and dS, then dV^T += dO^T P
-        // and dK^T += Q^T dS.
+        // S and dP for both 32-query halves, then per half P and dS,
+        // dV^T += dO^T P and dK^T += Q^T dS.
+        f32x16 svs[2], dps[2];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            f32x16 sv = half_product<D, D == 128>(qt_l, kf, blk, n, h);
-            f32x16 dp = half_product<D, D == 128>(gt_l, vf, blk, n, h);
+            svs[blk] = half_product<D, D == 128>(qt_l, kf, blk, n, h);
+            dps[blk] = half_product<D, D == 128>(gt_l, vf, blk, n, h);
+        }
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            f32x16& sv = svs[blk];
+            f32x16& dp = dps[blk];
 #pragma unroll
             for (int r4 = 0; r4 < 16; r4 += 4) {
                 const int x0 = reg_row(blk, r4, h);
@@ -713,6 +719,17 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kern
             }
             half_accumulate_tr<D, D == 128>(dv, gt_l, sv, blk, lane);
             half_accumulate_tr<D, D == 128>(dk, qt_l, dp, blk, lane);
+        }
+        // At d = 128 (one wave per SIMD) the MFMAs of the second half's
+        // products and of both halves' accumulations are interleaved with
+        // the softmax arithmetic, so the matrix pipe and the vector ALU of
+        // the one wave run together.
+        if constexpr (D == 128) {
+#pragma unroll
+            for (int i = 0; i < 48; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+            }
         }
     };
 
