@@ -101,18 +101,18 @@ class PlanCache {
     }
 
     // The backward plan (key blocks -> query tiles) for (spec, T).
-    int get_bwd(const sa_mask& m, int T, sa::BwdDevicePlan* out) {
+    int get_bwd(const sa_mask& m, int T, int bkb, sa::BwdDevicePlan* out) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return SA_ERR_HIP;
-        std::string key = sa::canonical_spec(m) + "|T=" + std::to_string(T) + "|bwd|dev=" +
-                          std::to_string(dev);
+        std::string key = sa::canonical_spec(m) + "|T=" + std::to_string(T) + "|bwd|bkb=" +
+                          std::to_string(bkb) + "|dev=" + std::to_string(dev);
         std::lock_guard<std::mutex> lock(mu_);
         auto it = bwd_.find(key);
         if (it != bwd_.end()) {
             *out = it->second.plan;
             return SA_OK;
         }
-        sa::BwdHostPlan hp = sa::build_bwd_plan(MaskRule(m, T));
+        sa::BwdHostPlan hp = sa::build_bwd_plan(MaskRule(m, T), bkb);
         sa::BwdDevicePlan dp;
         dp.n_kb = hp.n_kb;
         size_t off = 0;
@@ -317,8 +317,8 @@ int backward(int dtype, const void* Q, const void* K, const void* V, const void*
     if (B < 1 || H < 1 || T < 1 || T > SA_MAX_T) return SA_ERR_SHAPE;
     if (!supported_d(d)) return SA_ERR_UNSUPPORTED;
     const int64_t BH = int64_t(B) * H;
-    const int64_t n_qb = (int64_t(T) + sa::kBQ - 1) / sa::kBQ;
-    const int64_t n_kb = (int64_t(T) + sa::kBKB - 1) / sa::kBKB;
+    const int64_t n_qb = (int64_t(T) + 64 - 1) / 64;    // the finer of the two plan shapes
+    const int64_t n_kb = (int64_t(T) + 64 - 1) / 64;
     if (BH > INT32_MAX || BH * n_qb > INT32_MAX || BH * n_kb > INT32_MAX) return SA_ERR_SHAPE;
     for (const void* p : {Q, K, V, O, dO, static_cast<const void*>(dQ), static_cast<const void*>(dK),
                           static_cast<const void*>(dV)})
@@ -338,11 +338,15 @@ int backward(int dtype, const void* Q, const void* K, const void* V, const void*
     sa_mask m;
     int rc = parse_for(spec, T, &m);
     if (rc != SA_OK) return rc;
+    // With the forward's 64-row plans (block mode, 64-key blocks, bf16 d=64)
+    // the backward uses 64-query blocks and 64-key blocks as well.
+    const int bq = sa::fwd_query_block(m, d, dtype);
+    const int bkb = bq == 64 ? 64 : sa::kBKB;
     DevicePlan dp;
-    rc = cache().get(m, T, sa::kBQ, &dp);
+    rc = cache().get(m, T, bq, &dp);
     if (rc != SA_OK) return rc;
     sa::BwdDevicePlan bp;
-    rc = cache().get_bwd(m, T, &bp);
+    rc = cache().get_bwd(m, T, bkb, &bp);
     if (rc != SA_OK) return rc;
     float* Dw = nullptr;
     rc = workspace().get(lbytes, stream, &Dw);
@@ -376,7 +380,7 @@ int backward(int dtype, const void* Q, const void* K, const void* V, const void*
     a.blk_ptr = reinterpret_cast<const int32_t*>(base + dp.off_blk_ptr);
     a.blk_iv = reinterpret_cast<const int32_t*>(base + dp.off_blk_iv);
     a.lse = nullptr;
-    a.bq = sa::kBQ;
+    a.bq = bq;
     b.dO = dO;
     b.lse = lse;
     b.dQ = dQ;

@@ -388,20 +388,21 @@ __device__ __forceinline__ int swz(int r) {
 // This wave's share of the direct loads of one 64-row tile of two [T][d]
 // tensors: LDS chunk position p of row r receives source chunk p ^ swz(r).
 // row_of(r) is the source row of tile row r (always a valid row).
-template <int D, typename RowOf>
+template <int D, int NW, typename RowOf>
 __device__ __forceinline__ void dma_rows2(__bf16* dst_a, __bf16* dst_b, const __bf16* src_a,
                                           const __bf16* src_b, RowOf row_of, int wave, int lane) {
-    constexpr int CPR = D / 8;       // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;    // rows per instruction
-    constexpr int NJ = CPR / kWaves; // instructions per wave
-    // Instruction j of this wave fills tile rows r0 + j * kWaves * RPI; the
-    // row's low four bits, hence its swizzle, do not depend on j.
+    constexpr int CPR = D / 8;     // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;  // rows per instruction
+    constexpr int NJ = CPR / NW;   // instructions per wave (NW waves share the tile)
+    static_assert(CPR % NW == 0, "loads split evenly over the waves");
+    // Instruction j of this wave fills tile rows r0 + j * NW * RPI; the row's
+    // low four bits, hence its swizzle, do not depend on j.
     const int r0 = wave * RPI + lane / CPR;
     const int ch = (lane % CPR) ^ swz<D>(r0);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        const size_t off = size_t(row_of(r0 + j * kWaves * RPI)) * D + ch * 8;
-        const int lds = (wave + j * kWaves) * 512;
+        const size_t off = size_t(row_of(r0 + j * NW * RPI)) * D + ch * 8;
+        const int lds = (wave + j * NW) * 512;
         __builtin_amdgcn_global_load_lds(as_global(src_a + off), as_lds(dst_a + lds), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(as_global(src_b + off), as_lds(dst_b + lds), 16, 0, 0);
     }
@@ -518,8 +519,8 @@ __device__ __forceinline__ void bcur_advance(BwdCursor& c, const FwdArgs& a) {
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
     using E = __bf16;
     using S = Shape<E, D>;
     using F = typename Ops<E>::frag;
@@ -542,7 +543,7 @@ __global__ __launch_bounds__(kThreads, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
     const E* Vp = static_cast<const E*>(a.V) + base;
     const E* Op = static_cast<const E*>(a.O) + base;
     const E* Gp = static_cast<const E*>(b.dO) + base;
-    const int qi = qb * kBQ + wave * 32 + n;
+    const int qi = qb * (NW * 32) + wave * 32 + n;
 
     F qf[S::NKS], gf[S::NKS];
     load_frags<E, D>(qf, Qp, qi, T, h);
@@ -572,10 +573,10 @@ __global__ __launch_bounds__(kThreads, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
     auto issue = [&](const BwdCursor& c, E* kd, E* vd) {
         if (c.inplace()) {
             const int k0 = c.kb * kBK;
-            dma_rows2<D>(kd, vd, Kp, Vp, [&](int r) { return min(k0 + r, T - 1); }, wave, lane);
+            dma_rows2<D, NW>(kd, vd, Kp, Vp, [&](int r) { return min(k0 + r, T - 1); }, wave, lane);
         } else {
             const int g0 = c.gi;
-            dma_rows2<D>(kd, vd, Kp, Vp, [&](int r) { return gkey(min(g0 + r, gtot - 1)); }, wave, lane);
+            dma_rows2<D, NW>(kd, vd, Kp, Vp, [&](int r) { return gkey(min(g0 + r, gtot - 1)); }, wave, lane);
         }
     };
     auto compute = [&](const BwdCursor& c, const E* kt, const E* vt) {
@@ -621,8 +622,8 @@ __global__ __launch_bounds__(kThreads, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
     if (qi < T) store_rows<E, D>(static_cast<E*>(b.dQ) + base, acc, qi, h, b.scale);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kernel(BwdArgs b) {
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kernel(BwdArgs b) {
     using E = __bf16;
     using S = Shape<E, D>;
     using F = typename Ops<E>::frag;
@@ -649,7 +650,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kern
     const E* Gp = static_cast<const E*>(b.dO) + base;
     const float* Lp = b.lse + size_t(bh) * size_t(T);
     const float* Dp = b.Dw + size_t(bh) * size_t(T);
-    const int kj = kb * kBKB + wave * 32 + n;
+    const int kj = kb * (NW * 32) + wave * 32 + n;
 
     F kf[S::NKS], vf[S::NKS];
     load_frags<E, D>(kf, Kp, kj, T, h);
@@ -675,7 +676,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kern
     };
     enter();
     auto issue = [&](int q0, E* qd, E* gd, float* lsd, float* dsd) {
-        dma_rows2<D>(qd, gd, Qp, Gp, [&](int rr) { return min(q0 + rr, T - 1); }, wave, lane);
+        dma_rows2<D, NW>(qd, gd, Qp, Gp, [&](int rr) { return min(q0 + rr, T - 1); }, wave, lane);
         if (wave == 0) {
             const int i = min(q0 + lane, T - 1);
             __builtin_amdgcn_global_load_lds(as_global(Lp + i), as_lds(lsd), 4, 0, 0);
@@ -810,14 +811,16 @@ int launch_b(const BwdArgs& b, void* stream) {
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
-template <int D>
+// NW waves per workgroup: 4 (128-query and 128-key blocks) or 2 (the 64-row
+// plans of block mode).
+template <int D, int NW>
 int launch_b_dma(const BwdArgs& b, void* stream) {
-    const unsigned g1 = static_cast<unsigned>(int64_t(b.f.BH) * ((b.f.T + kBQ - 1) / kBQ));
-    hipLaunchKernelGGL((sa_bwd_dq_dma_kernel<D>), dim3(g1), dim3(kThreads), 0,
+    const unsigned g1 = static_cast<unsigned>(int64_t(b.f.BH) * ((b.f.T + NW * 32 - 1) / (NW * 32)));
+    hipLaunchKernelGGL((sa_bwd_dq_dma_kernel<D, NW>), dim3(g1), dim3(NW * 64), 0,
                        static_cast<hipStream_t>(stream), b);
     if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
     const unsigned g2 = static_cast<unsigned>(int64_t(b.f.BH) * b.n_kb);
-    hipLaunchKernelGGL((sa_bwd_dkv_dma_kernel<D>), dim3(g2), dim3(kThreads), 0,
+    hipLaunchKernelGGL((sa_bwd_dkv_dma_kernel<D, NW>), dim3(g2), dim3(NW * 64), 0,
                        static_cast<hipStream_t>(stream), b);
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
@@ -825,12 +828,13 @@ int launch_b_dma(const BwdArgs& b, void* stream) {
 }  // namespace
 
 int launch_bwd(int dtype, int d, const BwdArgs& b, void* stream) {
+    if (b.f.bq != kBQ && !(b.f.bq == 64 && dtype == SA_DTYPE_BF16 && d == 64)) return SA_ERR_UNSUPPORTED;
     if (dtype == SA_DTYPE_BF16) {
         switch (d) {
             case 16: return launch_b<__bf16, 16>(b, stream);
             case 32: return launch_b<__bf16, 32>(b, stream);
-            case 64: return launch_b_dma<64>(b, stream);
-            case 128: return launch_b_dma<128>(b, stream);
+            case 64: return b.f.bq == 64 ? launch_b_dma<64, 2>(b, stream) : launch_b_dma<64, 4>(b, stream);
+            case 128: return launch_b_dma<128, 4>(b, stream);
         }
     } else if (dtype == SA_DTYPE_F32) {
         switch (d) {

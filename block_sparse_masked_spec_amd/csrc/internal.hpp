@@ -176,7 +176,8 @@ struct BwdHostPlan {
     int64_t tiles = 0, masked_tiles = 0;
 };
 
-BwdHostPlan build_bwd_plan(const MaskRule& rule);
+// Key blocks of bkb keys (kBKB, or 64 with the forward's 64-row plans).
+BwdHostPlan build_bwd_plan(const MaskRule& rule, int32_t bkb);
 
 // Backward arguments: the forward's (rule, plan, Q, K, V, O) plus gradients,
 // the saved log-sum-exp and the transposed plan.

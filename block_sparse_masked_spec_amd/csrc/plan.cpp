@@ -244,17 +244,17 @@ HostPlan build_plan(const MaskRule& rule, int32_t bq, int32_t bk) {
     return p;
 }
 
-BwdHostPlan build_bwd_plan(const MaskRule& rule) {
+BwdHostPlan build_bwd_plan(const MaskRule& rule, int32_t bkb) {
     BwdHostPlan p;
     const int64_t T = rule.T();
-    p.n_kb = static_cast<int32_t>((T + kBKB - 1) / kBKB);
+    p.n_kb = static_cast<int32_t>((T + bkb - 1) / bkb);
     p.n_qt = static_cast<int32_t>((T + kBQB - 1) / kBQB);
     const bool any_global_row = rule.rows_global_in(0, T) > 0;
     const int64_t back = rule.band_back(), fwd = rule.band_fwd();
     std::vector<int64_t> work(p.n_kb, 0);
     p.kb_ptr.push_back(0);
     for (int32_t kb = 0; kb < p.n_kb; ++kb) {
-        const int64_t k0 = int64_t(kb) * kBKB, k1 = std::min<int64_t>(T, k0 + kBKB);
+        const int64_t k0 = int64_t(kb) * bkb, k1 = std::min<int64_t>(T, k0 + bkb);
         // Query tiles that can hold allowed pairs: every tile when some row is
         // global, the block has column keys or in block mode; else the rows
         // whose band meets the block.
@@ -273,7 +273,7 @@ BwdHostPlan build_bwd_plan(const MaskRule& rule) {
                 open = false;
                 continue;
             }
-            const bool need_mask = !(cls == SA_TILE_FULL && q0 + kBQB <= T && k0 + kBKB <= T);
+            const bool need_mask = !(cls == SA_TILE_FULL && q0 + kBQB <= T && k0 + bkb <= T);
             const int32_t flag = need_mask ? int32_t(0x80000000u) : 0;
             if (open && (p.kb_runs.back() & int32_t(0x80000000u)) == flag &&
                 (p.kb_runs.back() & 0x7fffffff) == qt) {

@@ -113,6 +113,18 @@ def test_backward_edge_lengths(gpu, T, dtype):
         full_check(gpu, spec, 1, 2, T, 64, dtype, seed=T)
 
 
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 130, 257])
+def test_backward_block_mode_64_row_tiles(gpu, T):
+    """Block mode with 64-key blocks at bf16 d = 64 runs the backward on
+    64-query and 64-key blocks (two waves per workgroup)."""
+    specs = ["blocks;block=64;radius=1;random=2;seed=4"]
+    if T >= 3:
+        specs.append("blocks;block=64;random=3;seed=1;stride=29;global=0:3")
+    for spec in specs:
+        assert gpu.sparse_attn_plan_info(spec, T, 64)["bq"] == 64
+        full_check(gpu, spec, 2, 2, T, 64, "bf16", seed=T)
+
 def test_backward_window_layer_2k(gpu):
     """B=1, H=4, T=2048, d=128, causal window 256: every gradient compared."""
     full_check(gpu, "causal;window=256", 1, 4, 2048, 128, "bf16", seed=3)
