@@ -137,3 +137,42 @@ def test_backward_is_deterministic(gpu):
     b = run(gpu, "causal;window=200;stride=64", q, k, v, g)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+
+def heads_check(gpu, spec, B, H, T, d, seed, heads, prefix=None, window=None):
+    """Full-size backward on the GPU, the listed (b, h) pairs checked
+    against the fp64 oracle: in full, or -- for a causal window w -- on the
+    first `prefix` rows.  Rows below the prefix read only keys below it, so
+    their LSE and dQ are exact on the prefix; keys j < prefix - w + 1 have
+    every row that reads them inside the prefix, so their dK, dV are too."""
+    q, k, v = inputs.qkv(B, H, T, d, "bf16", seed)
+    g = inputs.qkv(B, H, T, d, "bf16", seed + 500)[0]
+    o, lse, dq, dk, dv = run(gpu, spec, q, k, v, g)
+    L = prefix or T
+    kmax = L if prefix is None else L - window + 1
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1), slice(0, L))
+        qs, ks, vs, gs = (x[sl] for x in (q, k, v, g))
+        _, lse_ref, _ = oracle.forward_rows(spec, qs, ks, vs)
+        assert np.abs(lse[sl].double().numpy() - lse_ref).max() <= 2.0 ** -8, f"lse b={b} h={h}"
+        rq, rk, rv = oracle.backward(spec, qs, ks, vs, gs)
+        check_grad(dq[sl], rq, "bf16", f"dQ {spec} b={b} h={h}")
+        ksl = (slice(b, b + 1), slice(h, h + 1), slice(0, kmax))
+        check_grad(dk[ksl], rk[:, :, :kmax], "bf16", f"dK {spec} b={b} h={h}")
+        check_grad(dv[ksl], rv[:, :, :kmax], "bf16", f"dV {spec} b={b} h={h}")
+
+
+def test_backward_mistral_32k_window_full_size(gpu):
+    """The 32K-window layer at full size (B=1, H=32, T=32768, d=128), run on
+    the GPU in full; head 17 compared on its first 8192 rows (full windows
+    from row 4095 on) and the 4097 keys whose readers all lie there."""
+    heads_check(gpu, "causal;window=4096", 1, 32, 32768, 128, seed=0, heads=[(0, 17)],
+                prefix=8192, window=4096)
+
+
+def test_backward_bigbird_4k_full_size(gpu):
+    """The 4K BigBird layer at full size (B=8, H=12, T=4096, d=64, 64-row
+    plans): three (b, h) slices compared in full."""
+    spec = "blocks;block=64;radius=1;random=3;seed=0;global=0:128"
+    heads_check(gpu, spec, 8, 12, 4096, 64, seed=1, heads=[(0, 0), (3, 7), (7, 11)])
