@@ -365,6 +365,8 @@ def main():
     info = [sa.sparse_attn_plan_info(s, T, d, sa.SA_DTYPE_BF16 if dtype == "bf16" else sa.SA_DTYPE_F32)
             for s in specs]
     executed = sum(i["executed_cells"] for i in info) * B * H
+    # Plans that split heavy query blocks add a merge kernel to each call.
+    kernels = kernel_name(dtype, d) + (" + sa_fwd_merge_kernel" if any(i["split_parts"] for i in info) else "")
 
     stream = torch.cuda.current_stream()
 
@@ -399,7 +401,7 @@ def main():
     roofline = {
         "bound": bound, "achieved": achieved, "peak": pk, "unit": unit,
         "frac": achieved / pk, "traffic": traffic,
-        "kernel": kernel_name(dtype, d), "ms_per_launch": ms_per_launch,
+        "kernel": kernels, "ms_per_launch": ms_per_launch,
         "algorithmic_flops_per_step": flops, "algorithmic_bytes_per_step": alg_bytes,
         "executed_over_allowed": executed / (E_total if E_total else 1),
     }

@@ -66,7 +66,7 @@ class sa_plan_info(ctypes.Structure):
     _fields_ = [
         ("bq", ctypes.c_int32), ("bk", ctypes.c_int32),
         ("n_qb", ctypes.c_int32), ("n_kb", ctypes.c_int32),
-        ("subsequences", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("subsequences", ctypes.c_int32), ("split_parts", ctypes.c_int32),
         ("inplace_tiles", ctypes.c_int64), ("masked_tiles", ctypes.c_int64),
         ("gathered_tiles", ctypes.c_int64), ("gathered_keys", ctypes.c_int64),
         ("executed_cells", ctypes.c_int64), ("allowed_cells", ctypes.c_int64),

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -40,24 +41,36 @@ int parse_for(const char* spec, int T, sa_mask* m) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Tile cap of the fast path's work items: automatic, or SA_FWD_SPLIT_TILES=n
+// (n > 0) to split every query block above n tiles.
+int64_t split_cap() {
+    const char* e = getenv("SA_FWD_SPLIT_TILES");
+    const long long n = e ? atoll(e) : 0;
+    return n > 0 ? n : sa::kSplitAuto;
+}
+
 class PlanCache {
   public:
-    // Returns SA_OK and a device plan for (spec, T, bq) on the current device.
-    int get(const sa_mask& m, int T, int bq, DevicePlan* out) {
+    // Returns SA_OK and a device plan for (spec, T, bq) on the current device;
+    // split_cap as build_plan's.
+    int get(const sa_mask& m, int T, int bq, int64_t split_cap, DevicePlan* out) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return SA_ERR_HIP;
         std::string key = sa::canonical_spec(m) + "|T=" + std::to_string(T) + "|bq=" +
                           std::to_string(bq) + "|bk=" + std::to_string(sa::kBK) +
-                          "|dev=" + std::to_string(dev);
+                          "|split=" + std::to_string(split_cap) + "|dev=" + std::to_string(dev);
         std::lock_guard<std::mutex> lock(mu_);
         auto it = plans_.find(key);
         if (it != plans_.end()) {
             *out = it->second.plan;
             return SA_OK;
         }
-        HostPlan hp = sa::build_plan(MaskRule(m, T), bq, sa::kBK);
+        HostPlan hp = sa::build_plan(MaskRule(m, T), bq, sa::kBK, split_cap);
         DevicePlan dp;
         dp.n_qb = hp.n_qb;
+        dp.n_items = hp.n_items;
+        dp.n_parts = hp.n_parts;
+        dp.n_split = static_cast<int32_t>(hp.split_qb.size());
         size_t off = 0;
         auto section = [&](size_t bytes, size_t* where) {
             off = align_up(off, 16);
@@ -73,6 +86,10 @@ class PlanCache {
         section(hp.rowbits.size() * 4, &dp.off_rowbits);
         section(hp.blk_ptr.size() * 4, &dp.off_blk_ptr);
         section(hp.blk_iv.size() * 4, &dp.off_blk_iv);
+        section(hp.item_qb.size() * 4, &dp.off_item_qb);
+        section(hp.item_part.size() * 4, &dp.off_item_part);
+        section(hp.split_qb.size() * 4, &dp.off_split_qb);
+        section(hp.split_ptr.size() * 4, &dp.off_split_ptr);
         dp.bytes = align_up(off, 16) + 16;
         std::vector<unsigned char> host(dp.bytes, 0);
         auto put = [&](size_t where, const void* src, size_t bytes) {
@@ -87,6 +104,10 @@ class PlanCache {
         put(dp.off_rowbits, hp.rowbits.data(), hp.rowbits.size() * 4);
         put(dp.off_blk_ptr, hp.blk_ptr.data(), hp.blk_ptr.size() * 4);
         put(dp.off_blk_iv, hp.blk_iv.data(), hp.blk_iv.size() * 4);
+        put(dp.off_item_qb, hp.item_qb.data(), hp.item_qb.size() * 4);
+        put(dp.off_item_part, hp.item_part.data(), hp.item_part.size() * 4);
+        put(dp.off_split_qb, hp.split_qb.data(), hp.split_qb.size() * 4);
+        put(dp.off_split_ptr, hp.split_ptr.data(), hp.split_ptr.size() * 4);
         if (hipMalloc(&dp.base, dp.bytes) != hipSuccess) {
             (void)hipGetLastError();
             return SA_ERR_NOMEM;
@@ -269,10 +290,13 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     if (sub > 1) m.dilation = 1;
     const int Ts = T / sub;
     const int bq = sa::fwd_query_block(m, d, dtype);
-    if (BH * sub * ((int64_t(Ts) + bq - 1) / bq) > INT32_MAX) return SA_ERR_SHAPE;
+    // Only the bf16 fast path runs split plans (and leaves them for the
+    // merge kernel).
+    const bool fast = sa::fwd_fast_path(dtype, d, bq, sub);
     DevicePlan dp;
-    rc = cache().get(m, Ts, bq, &dp);
+    rc = cache().get(m, Ts, bq, fast && sub == 1 ? split_cap() : 0, &dp);
     if (rc != SA_OK) return rc;
+    if (BH * sub * int64_t(dp.n_items) > INT32_MAX) return SA_ERR_SHAPE;
     sa::FwdArgs a;
     a.Q = Q;
     a.K = K;
@@ -302,10 +326,22 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     a.blk_iv = reinterpret_cast<const int32_t*>(base + dp.off_blk_iv);
     a.lse = lse;
     a.bq = bq;
-    const int64_t grid = int64_t(a.BH) * dp.n_qb;
+    a.item_qb = reinterpret_cast<const int32_t*>(base + dp.off_item_qb);
+    a.item_part = dp.n_parts > 0 ? reinterpret_cast<const int32_t*>(base + dp.off_item_part) : nullptr;
+    a.part = nullptr;
+    a.n_parts = dp.n_parts;
+    if (dp.n_parts > 0) {
+        const size_t pbytes = size_t(a.BH) * dp.n_parts * bq * (size_t(d) + 2) * sizeof(float);
+        rc = workspace().get(pbytes, stream, &a.part);
+        if (rc != SA_OK) return rc;
+    }
+    const int64_t grid = int64_t(a.BH) * dp.n_items;
+    if (!fast) return sub == 1 ? sa::launch_fwd(dtype, d, a, grid, stream) : SA_ERR_UNSUPPORTED;
     int lrc = sa::launch_fwd_fast(dtype, d, a, grid, stream);
-    if (lrc == SA_ERR_UNSUPPORTED && sub == 1) lrc = sa::launch_fwd(dtype, d, a, grid, stream);
-    return lrc;
+    if (lrc != SA_OK || dp.n_parts == 0) return lrc;
+    return sa::launch_fwd_merge(d, a, reinterpret_cast<const int32_t*>(base + dp.off_split_qb),
+                                reinterpret_cast<const int32_t*>(base + dp.off_split_ptr), dp.n_split,
+                                stream);
 }
 
 // Forward arguments for (spec, T, d): parse, plan lookup and the rule fields.
@@ -343,7 +379,7 @@ int backward(int dtype, const void* Q, const void* K, const void* V, const void*
     const int bq = sa::fwd_query_block(m, d, dtype);
     const int bkb = bq == 64 ? 64 : sa::kBKB;
     DevicePlan dp;
-    rc = cache().get(m, T, bq, &dp);
+    rc = cache().get(m, T, bq, 0, &dp);
     if (rc != SA_OK) return rc;
     sa::BwdDevicePlan bp;
     rc = cache().get_bwd(m, T, bkb, &bp);
@@ -381,6 +417,10 @@ int backward(int dtype, const void* Q, const void* K, const void* V, const void*
     a.blk_iv = reinterpret_cast<const int32_t*>(base + dp.off_blk_iv);
     a.lse = nullptr;
     a.bq = bq;
+    a.item_qb = nullptr;
+    a.item_part = nullptr;
+    a.part = nullptr;
+    a.n_parts = 0;
     b.dO = dO;
     b.lse = lse;
     b.dQ = dQ;
@@ -588,13 +628,15 @@ SA_EXPORT int sparse_attn_plan_info(const char* mask_spec, int T, int d, int dty
         if (sub > 1) mp.dilation = 1;
         MaskRule prule(mp, T / sub);
         bq = sa::fwd_query_block(mp, d, dtype);
-        HostPlan hp = sa::build_plan(prule, bq, bk);
+        HostPlan hp = sa::build_plan(prule, bq, bk,
+                                     sub == 1 && sa::fwd_fast_path(dtype, d, bq, sub) ? split_cap() : 0);
         std::memset(info, 0, sizeof(*info));
         info->bq = bq;
         info->bk = bk;
         info->n_qb = hp.n_qb;
         info->n_kb = hp.n_kb;
         info->subsequences = sub;
+        info->split_parts = hp.n_parts;
         info->inplace_tiles = hp.inplace_tiles * sub;
         info->masked_tiles = hp.masked_tiles * sub;
         info->gathered_tiles = hp.gathered_tiles * sub;

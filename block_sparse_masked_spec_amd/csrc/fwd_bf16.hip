@@ -328,9 +328,10 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, h = lane >> 5;
     const int work = xcd_slice_index(blockIdx.x, gridDim.x);
-    const int n_qb = gridDim.x / a.BH;
-    const int bh = work / n_qb;
-    const int qb = ldc(a.qb_order, work % n_qb);
+    const int n_items = gridDim.x / a.BH;
+    const int bh = work / n_items;
+    const int it = ldc(a.qb_order, work % n_items);  // work item: a query block or part of one
+    const int qb = ldc(a.item_qb, it);
     const int T = a.T;
     // Row stride and base of this sequence; with SUB, sequence bh is residue
     // class bh % sub of the full sequence bh / sub.
@@ -365,10 +366,10 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
         qblk[g] = a.blk > 0 ? min(qi, T - 1) / a.blk : 0;
     }
 
-    const int ga0 = ldc(a.gseg, 4 * qb), ga1 = ldc(a.gseg, 4 * qb + 1);
-    const int gb0 = ldc(a.gseg, 4 * qb + 2), gb1 = ldc(a.gseg, 4 * qb + 3);
+    const int ga0 = ldc(a.gseg, 4 * it), ga1 = ldc(a.gseg, 4 * it + 1);
+    const int gb0 = ldc(a.gseg, 4 * it + 2), gb1 = ldc(a.gseg, 4 * it + 3);
     const int gna = ga1 - ga0;
-    Cursor cur{ldc(a.run_ptr, qb), ldc(a.run_ptr, qb + 1), 0, 0, false, 0, gna + (gb1 - gb0)};
+    Cursor cur{ldc(a.run_ptr, it), ldc(a.run_ptr, it + 1), 0, 0, false, 0, gna + (gb1 - gb0)};
     cursor_enter_run(cur, a);
 
     auto run_tile = [&](const Cursor& c, const char* kt, const char* vt) {
@@ -404,13 +405,37 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
         cur = nxt;
     }
 
-    // Epilogue: O = acc / l (both lane halves' sums).
+    // Epilogue: O = acc / l (both lane halves' sums), or -- for one part of
+    // a split block -- acc, the running max and l into the item's slot.
+    const int part = a.item_part ? ldc(a.item_part, it) : -1;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const int qi = q_base + g * 32 + n;
         const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.l_run[g]),
                                                          __float_as_uint(st.l_run[g]), false, false);
         const float lt = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+        if (part >= 0) {
+            const size_t slot = (size_t(bh) * a.n_parts + part) * BQ + (qi - qb * BQ);
+            float* po = a.part + slot * D;
+#pragma unroll
+            for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    float4 q;
+                    q.x = st.acc[g][db][r4 * 4];
+                    q.y = st.acc[g][db][r4 * 4 + 1];
+                    q.z = st.acc[g][db][r4 * 4 + 2];
+                    q.w = st.acc[g][db][r4 * 4 + 3];
+                    *reinterpret_cast<float4*>(po + db * 32 + r4 * 8 + h * 4) = q;
+                }
+            if (h == 0) {
+                float2 ml;
+                ml.x = st.m_run[g];
+                ml.y = lt;
+                reinterpret_cast<float2*>(a.part + size_t(a.BH) * a.n_parts * BQ * D)[slot] = ml;
+            }
+            continue;
+        }
         const float inv = 1.f / lt;
         if (a.lse && qi < T && h == 0) {  // log-sum-exp: the scores are in log2 units
             const size_t row = SUB ? size_t(bh / a.sub) * size_t(T) * a.sub + size_t(bh % a.sub) +
@@ -433,6 +458,51 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
     }
 }
 
+// Merge of a split block's partial slots, one workgroup per (sequence, split
+// block).  With m_p and l_p the part's reference max (log2 units) and row
+// sum and acc_p its unnormalised output, the row's result is
+// sum_p 2^(m_p - m) acc_p / sum_p 2^(m_p - m) l_p for m = max_p m_p: the
+// online softmax's own rescaling, applied across parts (a part without an
+// allowed key for the row has l_p = 0, acc_p = 0).
+template <int D>
+__global__ __launch_bounds__(256) void sa_fwd_merge_kernel(FwdArgs a, const int32_t* split_qb,
+                                                            const int32_t* split_ptr, int n_split) {
+    const int bh = blockIdx.x / n_split, sidx = blockIdx.x % n_split;
+    const int qb = split_qb[sidx], p0 = split_ptr[sidx], p1 = split_ptr[sidx + 1];
+    const int BQ = a.bq, T = a.T;
+    constexpr int C = D / 4;  // float4 pieces per row
+    const float* po = a.part;
+    const float2* pml = reinterpret_cast<const float2*>(a.part + size_t(a.BH) * a.n_parts * BQ * D);
+    __bf16* Op = static_cast<__bf16*>(a.O) + size_t(bh) * size_t(T) * D;
+    for (int t = threadIdx.x; t < BQ * C; t += blockDim.x) {
+        const int r = t / C, c = t % C;
+        const int qi = qb * BQ + r;
+        if (qi >= T) break;  // rows ascend with t
+        float m = -INFINITY;
+        for (int p = p0; p < p1; ++p) m = fmaxf(m, pml[(size_t(bh) * a.n_parts + p) * BQ + r].x);
+        float l = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+        for (int p = p0; p < p1; ++p) {
+            const size_t slot = (size_t(bh) * a.n_parts + p) * BQ + r;
+            const float2 ml = pml[slot];
+            const float w = __builtin_amdgcn_exp2f(ml.x - m);
+            const float4 v = *reinterpret_cast<const float4*>(po + slot * D + c * 4);
+            l = fmaf(w, ml.y, l);
+            o0 = fmaf(w, v.x, o0);
+            o1 = fmaf(w, v.y, o1);
+            o2 = fmaf(w, v.z, o2);
+            o3 = fmaf(w, v.w, o3);
+        }
+        const float inv = 1.f / l;
+        bf16x4 q;
+        q[0] = static_cast<__bf16>(o0 * inv);
+        q[1] = static_cast<__bf16>(o1 * inv);
+        q[2] = static_cast<__bf16>(o2 * inv);
+        q[3] = static_cast<__bf16>(o3 * inv);
+        *reinterpret_cast<bf16x4*>(Op + size_t(qi) * D + c * 4) = q;
+        if (a.lse && c == 0) a.lse[size_t(bh) * T + qi] = (m + __log2f(l)) * 0.6931471805599453f;
+    }
+}
+
 template <int D, int NG, int NW, bool SUB = false>
 int launch_t(const FwdArgs& a, int64_t grid, void* stream) {
     hipLaunchKernelGGL((sa_fwd_bf16_kernel<D, NG, NW, SUB>), dim3(static_cast<unsigned>(grid)),
@@ -451,6 +521,21 @@ int fast_variant() {
 }
 
 }  // namespace
+
+int launch_fwd_merge(int d, const FwdArgs& a, const int32_t* split_qb, const int32_t* split_ptr,
+                     int32_t n_split, void* stream) {
+    if (n_split <= 0 || a.sub != 1) return SA_ERR_UNSUPPORTED;
+    const dim3 grid(static_cast<unsigned>(int64_t(a.BH) * n_split));
+    if (d == 128)
+        hipLaunchKernelGGL(sa_fwd_merge_kernel<128>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a,
+                           split_qb, split_ptr, n_split);
+    else if (d == 64)
+        hipLaunchKernelGGL(sa_fwd_merge_kernel<64>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a,
+                           split_qb, split_ptr, n_split);
+    else
+        return SA_ERR_UNSUPPORTED;
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
 
 // Returns SA_ERR_UNSUPPORTED when (dtype, d) has no fast path.
 int launch_fwd_fast(int dtype, int d, const FwdArgs& a, int64_t grid, void* stream) {

@@ -93,12 +93,21 @@ class MaskRule {
 };
 
 // Execution plan for one (spec, T, tile shape).  All counts per (b, h).
+// The kernels run work items: each is one query block, or -- for a block
+// whose tile count is far above the mean -- one range of its tiles, whose
+// unnormalised result goes to a partial slot that a merge kernel combines.
 struct HostPlan {
     int32_t bq = 0, bk = 0, n_qb = 0, n_kb = 0;
-    std::vector<int32_t> qb_order;  // query blocks, most work first
-    std::vector<int32_t> run_ptr;   // n_qb + 1
+    int32_t n_items = 0;            // work items (n_qb when nothing is split)
+    int32_t n_parts = 0;            // items that write partial slots
+    std::vector<int32_t> qb_order;  // work items, most work first
+    std::vector<int32_t> run_ptr;   // n_items + 1
     std::vector<int32_t> runs;      // pairs: kb_begin, kb_end | (needs_mask << 31)
-    std::vector<int32_t> gseg;      // 4 per qb: [a0, a1) and [b0, b1) into colkeys
+    std::vector<int32_t> gseg;      // 4 per item: [a0, a1) and [b0, b1) into colkeys
+    std::vector<int32_t> item_qb;   // query block of each item
+    std::vector<int32_t> item_part; // -1 (writes O) or the item's partial slot
+    std::vector<int32_t> split_qb;  // the split query blocks ...
+    std::vector<int32_t> split_ptr; // ... and their slots [split_ptr[s], split_ptr[s+1])
     std::vector<int32_t> colkeys;   // sorted keys that are strided or global
     std::vector<uint64_t> colbits;  // bit j%64 of word j/64: key j is a colkey
     std::vector<uint32_t> rowbits;  // bit i%32 of word i/32: row i is global
@@ -107,15 +116,21 @@ struct HostPlan {
     int64_t inplace_tiles = 0, masked_tiles = 0, gathered_tiles = 0, gathered_keys = 0;
 };
 
-HostPlan build_plan(const MaskRule& rule, int32_t bq, int32_t bk);
+// split_cap: 0 = one item per query block; kSplitAuto = split blocks above
+// max(kSplitMinTiles, twice the mean tile count); n > 0 = split blocks above
+// n tiles.  A block of w > cap tiles becomes ceil(w / cap) items.
+constexpr int64_t kSplitMinTiles = 16;
+constexpr int64_t kSplitAuto = -1;
+HostPlan build_plan(const MaskRule& rule, int32_t bq, int32_t bk, int64_t split_cap = 0);
 
 // Device-resident plan: one allocation, section offsets in bytes.
 struct DevicePlan {
     void* base = nullptr;
     size_t bytes = 0;
-    int32_t n_qb = 0;
+    int32_t n_qb = 0, n_items = 0, n_parts = 0, n_split = 0;
     size_t off_qb_order = 0, off_run_ptr = 0, off_runs = 0, off_gseg = 0, off_colkeys = 0,
-           off_colbits = 0, off_rowbits = 0, off_blk_ptr = 0, off_blk_iv = 0;
+           off_colbits = 0, off_rowbits = 0, off_blk_ptr = 0, off_blk_iv = 0, off_item_qb = 0,
+           off_item_part = 0, off_split_qb = 0, off_split_ptr = 0;
 };
 
 // Device-resident backward plan (one allocation).
@@ -158,6 +173,13 @@ struct FwdArgs {
     const uint32_t* rowbits;
     float* lse;  // optional [BH][T] output: natural-log sum of exp of the row's scores
     int32_t bq;  // query rows per tile of the plan (kBQ, or 64: fast path only)
+    // Split plans (fast path only): item -> query block and partial slot.
+    // part holds [BH][n_parts][bq][d] fp32 unnormalised outputs, then
+    // [BH][n_parts][bq] float2 (running max in log2 units, row sum).
+    const int32_t* item_qb;    // null: item = query block
+    const int32_t* item_part;  // null: no partial slots
+    float* part;
+    int32_t n_parts;
 };
 
 constexpr int kBQ = 128;
@@ -235,9 +257,20 @@ inline int fwd_query_block(const sa_mask& m, int d, int dtype) {
                : kBQ;
 }
 
+// Whether the bf16 fast path runs (dtype, d) with bq-row tiles and `sub`
+// interleaved subsequences; only its plans are split.
+inline bool fwd_fast_path(int dtype, int d, int bq, int sub) {
+    if (dtype != SA_DTYPE_BF16 || (d != 64 && d != 128)) return false;
+    if (bq == 64) return d == 64 && sub == 1;
+    return bq == kBQ;
+}
+
 // Launch the fused forward kernel; returns SA_OK or SA_ERR_HIP.
 int launch_fwd(int dtype, int d, const FwdArgs& args, int64_t grid, void* stream);
 // The bf16 fast path (d = 64 or 128); SA_ERR_UNSUPPORTED for other shapes.
 int launch_fwd_fast(int dtype, int d, const FwdArgs& args, int64_t grid, void* stream);
+// Merge the partial slots of the n_split split query blocks into O (and LSE).
+int launch_fwd_merge(int d, const FwdArgs& args, const int32_t* split_qb, const int32_t* split_ptr,
+                     int32_t n_split, void* stream);
 
 }  // namespace sa

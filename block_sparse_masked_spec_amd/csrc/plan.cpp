@@ -159,7 +159,45 @@ int MaskRule::classify(int64_t q0, int64_t q1, int64_t k0, int64_t k1) const {
     return allowed == 0 ? SA_TILE_EMPTY : (allowed == cells ? SA_TILE_FULL : SA_TILE_PARTIAL);
 }
 
-HostPlan build_plan(const MaskRule& rule, int32_t bq, int32_t bk) {
+namespace {
+
+// The tiles of one query block: in-place runs, then its gathered keys
+// (segments [a0, a1) and [b0, b1) of colkeys, taken in that order).
+struct BlockTiles {
+    std::vector<int32_t> runs;  // pairs, as HostPlan::runs
+    int32_t a0 = 0, a1 = 0, b0 = 0, b1 = 0;
+    int64_t inplace = 0, gathered = 0;
+    int64_t work() const { return inplace + gathered; }
+};
+
+// Emit tiles [t0, t1) of block `bt` (in-place tiles first, then gathered
+// tiles of bk keys) as one work item's runs and gather segments.
+void emit_item(const BlockTiles& bt, int64_t t0, int64_t t1, int32_t bk, HostPlan& p) {
+    int64_t t = 0;  // tile index of the current run's first tile
+    for (size_t r = 0; r < bt.runs.size(); r += 2) {
+        const int32_t kb0 = bt.runs[r], end = bt.runs[r + 1];
+        const int32_t kb1 = end & 0x7fffffff, flag = end & int32_t(0x80000000u);
+        const int64_t lo = std::max<int64_t>(t0, t), hi = std::min<int64_t>(t1, t + (kb1 - kb0));
+        if (lo < hi) {
+            p.runs.push_back(static_cast<int32_t>(kb0 + (lo - t)));
+            p.runs.push_back(static_cast<int32_t>(kb0 + (hi - t)) | flag);
+        }
+        t += kb1 - kb0;
+    }
+    p.run_ptr.push_back(static_cast<int32_t>(p.runs.size() / 2));
+    // Gathered tiles [g0, g1) of the block, as a range of its key list.
+    const int64_t na = bt.a1 - bt.a0, nk = na + (bt.b1 - bt.b0);
+    const int64_t g0 = std::max<int64_t>(t0 - bt.inplace, 0), g1 = std::max<int64_t>(t1 - bt.inplace, 0);
+    const int64_t s = std::min(g0 * bk, nk), e = std::min(g1 * bk, nk);
+    p.gseg.push_back(static_cast<int32_t>(bt.a0 + std::min(s, na)));
+    p.gseg.push_back(static_cast<int32_t>(bt.a0 + std::min(e, na)));
+    p.gseg.push_back(static_cast<int32_t>(bt.b0 + std::max(s, na) - na));
+    p.gseg.push_back(static_cast<int32_t>(bt.b0 + std::max(e, na) - na));
+}
+
+}  // namespace
+
+HostPlan build_plan(const MaskRule& rule, int32_t bq, int32_t bk, int64_t split_cap) {
     HostPlan p;
     const int64_t T = rule.T();
     p.bq = bq;
@@ -177,10 +215,10 @@ HostPlan build_plan(const MaskRule& rule, int32_t bq, int32_t bk) {
     }
     p.blk_ptr = rule.iv_ptr();
     p.blk_iv = rule.ivals();
-    std::vector<int64_t> work(p.n_qb, 0);
-    p.run_ptr.push_back(0);
-    p.gseg.resize(4 * static_cast<size_t>(p.n_qb));
+    std::vector<BlockTiles> blocks(p.n_qb);
+    int64_t total_work = 0;
     for (int32_t qb = 0; qb < p.n_qb; ++qb) {
+        BlockTiles& bt = blocks[qb];
         const int64_t q0 = int64_t(qb) * bq, q1 = std::min<int64_t>(T, q0 + bq);
         int64_t klo, khi;
         if (rule.rows_global_in(q0, q1) > 0) {
@@ -191,7 +229,6 @@ HostPlan build_plan(const MaskRule& rule, int32_t bq, int32_t bk) {
             khi = rule.band_hi(q1 - 1);
         }
         const int64_t kb_lo = klo / bk, kb_hi = khi / bk + 1;
-        int64_t tiles = 0;
         bool open = false;
         for (int64_t kb = kb_lo; kb < kb_hi; ++kb) {
             const int cls = rule.classify(q0, q1, kb * bk, (kb + 1) * bk);
@@ -201,18 +238,17 @@ HostPlan build_plan(const MaskRule& rule, int32_t bq, int32_t bk) {
             }
             const bool need_mask = !(cls == SA_TILE_FULL && (kb + 1) * bk <= T);
             const int32_t flag = need_mask ? int32_t(0x80000000u) : 0;
-            if (open && (p.runs.back() & int32_t(0x80000000u)) == flag &&
-                (p.runs.back() & 0x7fffffff) == kb) {
-                p.runs.back() = int32_t(kb + 1) | flag;
+            if (open && (bt.runs.back() & int32_t(0x80000000u)) == flag &&
+                (bt.runs.back() & 0x7fffffff) == kb) {
+                bt.runs.back() = int32_t(kb + 1) | flag;
             } else {
-                p.runs.push_back(static_cast<int32_t>(kb));
-                p.runs.push_back(int32_t(kb + 1) | flag);
+                bt.runs.push_back(static_cast<int32_t>(kb));
+                bt.runs.push_back(int32_t(kb + 1) | flag);
                 open = true;
             }
-            ++tiles;
+            ++bt.inplace;
             p.masked_tiles += need_mask ? 1 : 0;
         }
-        p.run_ptr.push_back(static_cast<int32_t>(p.runs.size() / 2));
         // Gathered keys: strided/global keys outside [kb_lo*bk, kb_hi*bk)
         // that some row of the block may read.  Below the block's band every
         // such key precedes every row (causal holds); above it only bidir
@@ -222,25 +258,50 @@ HostPlan build_plan(const MaskRule& rule, int32_t bq, int32_t bk) {
             return static_cast<int32_t>(
                 std::lower_bound(p.colkeys.begin(), p.colkeys.end(), key) - p.colkeys.begin());
         };
-        const int32_t a0 = 0, a1 = first_at_or_after(kb_lo * bk);
-        int32_t b0 = first_at_or_after(kb_hi * bk), b1 = first_at_or_after(limit + 1);
-        if (b1 < b0) b1 = b0;
-        int32_t* g = &p.gseg[4 * static_cast<size_t>(qb)];
-        g[0] = a0;
-        g[1] = a1;
-        g[2] = b0;
-        g[3] = b1;
-        const int64_t nkeys = int64_t(a1 - a0) + (b1 - b0);
-        const int64_t gt = (nkeys + bk - 1) / bk;
-        p.inplace_tiles += tiles;
-        p.gathered_tiles += gt;
+        bt.a0 = 0;
+        bt.a1 = first_at_or_after(kb_lo * bk);
+        bt.b0 = first_at_or_after(kb_hi * bk);
+        bt.b1 = std::max(bt.b0, first_at_or_after(limit + 1));
+        const int64_t nkeys = int64_t(bt.a1 - bt.a0) + (bt.b1 - bt.b0);
+        bt.gathered = (nkeys + bk - 1) / bk;
+        p.inplace_tiles += bt.inplace;
+        p.gathered_tiles += bt.gathered;
         p.gathered_keys += nkeys;
-        work[qb] = tiles + gt;
+        total_work += bt.work();
     }
-    p.qb_order.resize(p.n_qb);
+    // Work items.  A block whose tile count is far above the mean (a block
+    // of global rows reads every key tile) would run alone long after the
+    // rest: a split plan makes it ceil(work / cap) items over consecutive
+    // tile ranges, each leaving an unnormalised partial result that a second
+    // kernel merges.
+    const int64_t mean = p.n_qb ? (total_work + p.n_qb - 1) / p.n_qb : 0;
+    const int64_t cap = split_cap == kSplitAuto ? std::max<int64_t>(kSplitMinTiles, 2 * mean)
+                        : split_cap > 0         ? split_cap
+                                                : INT64_MAX;
+    std::vector<int64_t> item_work;
+    p.run_ptr.push_back(0);
+    p.split_ptr.push_back(0);
+    for (int32_t qb = 0; qb < p.n_qb; ++qb) {
+        const BlockTiles& bt = blocks[qb];
+        const int64_t w = bt.work();
+        const int64_t parts = w > cap ? (w + cap - 1) / cap : 1;
+        for (int64_t x = 0; x < parts; ++x) {
+            const int64_t t0 = w * x / parts, t1 = w * (x + 1) / parts;
+            emit_item(bt, t0, t1, bk, p);
+            p.item_qb.push_back(qb);
+            p.item_part.push_back(parts > 1 ? p.n_parts++ : -1);
+            item_work.push_back(t1 - t0);
+        }
+        if (parts > 1) {
+            p.split_qb.push_back(qb);
+            p.split_ptr.push_back(p.n_parts);
+        }
+    }
+    p.n_items = static_cast<int32_t>(p.item_qb.size());
+    p.qb_order.resize(p.n_items);
     std::iota(p.qb_order.begin(), p.qb_order.end(), 0);
     std::stable_sort(p.qb_order.begin(), p.qb_order.end(),
-                     [&](int32_t x, int32_t y) { return work[x] > work[y]; });
+                     [&](int32_t x, int32_t y) { return item_work[x] > item_work[y]; });
     return p;
 }
 

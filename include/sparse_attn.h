@@ -137,7 +137,11 @@ typedef struct sa_plan_info {
                                     d in {64, 128}) runs as g interleaved
                                     plain windows of T/g rows; the tile
                                     counts below are totals over all g */
-    int32_t reserved;
+    int32_t split_parts;         /* bf16 fast path: work items that hold one
+                                    key range of a query block with far more
+                                    tiles than the mean (a block of global
+                                    rows); a merge kernel combines their
+                                    partial results.  0 when none is split */
     int64_t inplace_tiles;       /* contiguous key tiles executed */
     int64_t masked_tiles;        /* of those, tiles that evaluate the rule */
     int64_t gathered_tiles;      /* tiles of gathered landmark/global keys */

@@ -233,6 +233,53 @@ def test_cfg_gemma_interleave(gpu):
         sampled_check(gpu, spec, 2, 16, 8192, 128, seed=100 + layer, extra=(1023, 1024, 1025))
 
 
+# ------------------------------------------------- split query blocks (merge)
+def lse_check(sa, spec, B, H, T, d, seed):
+    """Forward with LSE on the GPU against the oracle: O to the bf16 bound,
+    LSE to 2^-8 (the scores are bf16 products summed in fp32)."""
+    q, k, v = inputs.qkv(B, H, T, d, "bf16", seed)
+    announce(f"fwd_lse bf16 B={B} H={H} T={T} d={d} spec={spec}")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    od = torch.empty_like(qd)
+    lse = torch.empty(B, H, T, dtype=torch.float32, device="cuda")
+    sa.sparse_attn_fwd_lse(qd, kd, vd, od, lse, B, H, T, d, spec)
+    torch.cuda.synchronize()
+    ref, lse_ref, _ = oracle.forward_rows(spec, q, k, v)
+    check_bf16(od.cpu(), ref, f"{spec} T={T} d={d}")
+    err = np.abs(lse.cpu().double().numpy() - lse_ref).max()
+    assert err <= 2.0 ** -8, f"lse err {err:.3e} {spec}"
+
+
+SPLIT_SPECS = [
+    ("bidir;radius=64;stride=16;phase=0;global=0:128", 1000, 64),
+    ("causal;window=64;stride=8;phase=3;global=5:9", 700, 128),
+    ("causal;window=100;global=300:340", 650, 128),
+    ("bidir;radius=40;stride=5;phase=1", 450, 64),
+    ("blocks;block=64;radius=1;random=3;seed=0;global=0:128", 1000, 64),
+]
+
+
+@pytest.mark.parametrize("cap", [1, 2, 3])
+@pytest.mark.parametrize("spec,T,d", SPLIT_SPECS)
+def test_split_blocks_forced(gpu, monkeypatch, spec, T, d, cap):
+    """Every query block above `cap` tiles split into key-range items and
+    merged: in-place runs cut mid-run and gathered key lists cut at any
+    tile, against the oracle (O and LSE)."""
+    monkeypatch.setenv("SA_FWD_SPLIT_TILES", str(cap))
+    info = gpu.sparse_attn_plan_info(spec, T, d)
+    assert info["split_parts"] > 0
+    lse_check(gpu, spec, 2, 3, T, d, seed=cap)
+
+
+def test_split_blocks_automatic(gpu):
+    """Global rows in the middle of a causal window: their block (rows
+    2944..3071) reads keys 0..3071, 48 tiles, against about 3 for the rest,
+    so the plan cuts it above 16 tiles into 3 items by itself."""
+    spec = "causal;window=64;global=3000:3050"
+    assert gpu.sparse_attn_plan_info(spec, 5000, 128)["split_parts"] == 3
+    lse_check(gpu, spec, 1, 2, 5000, 128, seed=3)
+
+
 # --------------------------------------------------------------- behaviour
 def test_deterministic_reruns(gpu):
     q, k, v = inputs.qkv(1, 8, 2048, 128, "bf16", 3)

@@ -239,6 +239,24 @@ def test_plan_window_overhead():
     assert info["executed_cells"] / info["allowed_cells"] < 1.05
 
 
+def test_plan_splits_blocks_of_global_rows(monkeypatch):
+    """Longformer 16K at d = 64: the block of global rows 0..127 reads all 256
+    key tiles, the mean block ceil(3800 / 128) = 30, so the fast path's plan
+    cuts it above 2 x 30 = 60 tiles into ceil(256 / 60) = 5 items.  Uniform
+    windows are never split, nor plans of the generic (fp32) kernel; the cap
+    can be forced."""
+    spec, T = "bidir;radius=256;stride=16;phase=0;global=0:128", 16384
+    info = sa.sparse_attn_plan_info(spec, T, 64)
+    assert info["inplace_tiles"] + info["gathered_tiles"] == 3800
+    assert info["split_parts"] == 5
+    assert sa.sparse_attn_plan_info(spec, T, 64, sa.SA_DTYPE_F32)["split_parts"] == 0
+    assert sa.sparse_attn_plan_info("causal;window=4096", 32768, 128)["split_parts"] == 0
+    monkeypatch.setenv("SA_FWD_SPLIT_TILES", "100")
+    assert sa.sparse_attn_plan_info(spec, T, 64)["split_parts"] == 3
+    # splitting moves work between items; the executed tiles stay the same
+    assert sa.sparse_attn_plan_info(spec, T, 64)["executed_cells"] == info["executed_cells"]
+
+
 # ------------------------------------------------------------ argument errors
 def test_plan_info_of_dilated_windows():
     """A pure dilated window with T a multiple of g runs as g plain windows
