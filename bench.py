@@ -99,8 +99,9 @@ def bwd_kernel_names(dtype: str, d: int) -> str:
     return "sa_bwd_dq_kernel + sa_bwd_dkv_kernel"
 
 
-def load_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, or None."""
+def load_counter(workload: str, field: str = "hbm_bytes_per_launch"):
+    """A figure from the committed counter summary (HBM bytes per launch, or
+    the MFMA-busy fraction), or None once the kernel source has changed."""
     try:
         data = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -108,7 +109,11 @@ def load_traffic(workload: str):
     entry = data.get(workload)
     if not entry or entry.get("kernel_sha") != kernel_sha(WORKLOADS[workload]):
         return None
-    return entry.get("hbm_bytes_per_launch")
+    return entry.get(field)
+
+
+def load_traffic(workload: str):
+    return load_counter(workload)
 
 
 def cpu_baseline(wl, specs, q, k, v, budget_s: float):
@@ -227,6 +232,7 @@ def backward_bench(args, wl):
         "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / BF16_PEAK_TFLOPS, "traffic": load_traffic(args.workload),
                      "kernel": bwd_kernel_names(wl["dtype"], d), "ms_per_launch": ms,
+                     "mfma_busy": load_counter(args.workload, "mfma_busy"),
                      "algorithmic_flops_per_step": flops, "algorithmic_bytes_per_step": alg_bytes},
         "cpu_baseline": None,
     }
@@ -402,6 +408,7 @@ def main():
         "bound": bound, "achieved": achieved, "peak": pk, "unit": unit,
         "frac": achieved / pk, "traffic": traffic,
         "kernel": kernels, "ms_per_launch": ms_per_launch,
+        "mfma_busy": load_counter(args.workload, "mfma_busy"),
         "algorithmic_flops_per_step": flops, "algorithmic_bytes_per_step": alg_bytes,
         "executed_over_allowed": executed / (E_total if E_total else 1),
     }

@@ -458,49 +458,55 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
     }
 }
 
-// Merge of a split block's partial slots, one workgroup per (sequence, split
-// block).  With m_p and l_p the part's reference max (log2 units) and row
-// sum and acc_p its unnormalised output, the row's result is
-// sum_p 2^(m_p - m) acc_p / sum_p 2^(m_p - m) l_p for m = max_p m_p: the
-// online softmax's own rescaling, applied across parts (a part without an
-// allowed key for the row has l_p = 0, acc_p = 0).
+// Merge of a split block's partial slots: one thread per (row, 4 columns),
+// 256 / (D/4) rows per workgroup.  With m_p and l_p the part's reference max
+// (log2 units) and row sum and acc_p its unnormalised output, the row's
+// result is sum_p 2^(m_p - m) acc_p / sum_p 2^(m_p - m) l_p for
+// m = max_p m_p: the online softmax's own rescaling, applied across parts (a
+// part without an allowed key for the row has l_p = 0, acc_p = 0).
+template <int D>
+struct MergeShape {
+    static constexpr int C = D / 4;      // float4 pieces per row
+    static constexpr int RPW = 256 / C;  // rows per workgroup
+};
+
 template <int D>
 __global__ __launch_bounds__(256) void sa_fwd_merge_kernel(FwdArgs a, const int32_t* split_qb,
                                                             const int32_t* split_ptr, int n_split) {
-    const int bh = blockIdx.x / n_split, sidx = blockIdx.x % n_split;
-    const int qb = split_qb[sidx], p0 = split_ptr[sidx], p1 = split_ptr[sidx + 1];
+    using M = MergeShape<D>;
     const int BQ = a.bq, T = a.T;
-    constexpr int C = D / 4;  // float4 pieces per row
-    const float* po = a.part;
+    const int per_blk = BQ / M::RPW;  // workgroups per split block
+    const int x = blockIdx.x % per_blk, y = blockIdx.x / per_blk;
+    const int bh = y / n_split, sidx = y % n_split;
+    const int r = x * M::RPW + threadIdx.x / M::C, c = threadIdx.x % M::C;
+    const int qb = split_qb[sidx], p0 = split_ptr[sidx], p1 = split_ptr[sidx + 1];
+    const int qi = qb * BQ + r;
+    if (qi >= T) return;
     const float2* pml = reinterpret_cast<const float2*>(a.part + size_t(a.BH) * a.n_parts * BQ * D);
-    __bf16* Op = static_cast<__bf16*>(a.O) + size_t(bh) * size_t(T) * D;
-    for (int t = threadIdx.x; t < BQ * C; t += blockDim.x) {
-        const int r = t / C, c = t % C;
-        const int qi = qb * BQ + r;
-        if (qi >= T) break;  // rows ascend with t
-        float m = -INFINITY;
-        for (int p = p0; p < p1; ++p) m = fmaxf(m, pml[(size_t(bh) * a.n_parts + p) * BQ + r].x);
-        float l = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-        for (int p = p0; p < p1; ++p) {
-            const size_t slot = (size_t(bh) * a.n_parts + p) * BQ + r;
-            const float2 ml = pml[slot];
-            const float w = __builtin_amdgcn_exp2f(ml.x - m);
-            const float4 v = *reinterpret_cast<const float4*>(po + slot * D + c * 4);
-            l = fmaf(w, ml.y, l);
-            o0 = fmaf(w, v.x, o0);
-            o1 = fmaf(w, v.y, o1);
-            o2 = fmaf(w, v.z, o2);
-            o3 = fmaf(w, v.w, o3);
-        }
-        const float inv = 1.f / l;
-        bf16x4 q;
-        q[0] = static_cast<__bf16>(o0 * inv);
-        q[1] = static_cast<__bf16>(o1 * inv);
-        q[2] = static_cast<__bf16>(o2 * inv);
-        q[3] = static_cast<__bf16>(o3 * inv);
-        *reinterpret_cast<bf16x4*>(Op + size_t(qi) * D + c * 4) = q;
-        if (a.lse && c == 0) a.lse[size_t(bh) * T + qi] = (m + __log2f(l)) * 0.6931471805599453f;
+    const size_t slot0 = size_t(bh) * a.n_parts * BQ + r;  // slot of part p: slot0 + p * BQ
+    float m = -INFINITY;
+    for (int p = p0; p < p1; ++p) m = fmaxf(m, pml[slot0 + size_t(p) * BQ].x);
+    float l = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    for (int p = p0; p < p1; ++p) {
+        const size_t slot = slot0 + size_t(p) * BQ;
+        const float2 ml = pml[slot];
+        const float w = __builtin_amdgcn_exp2f(ml.x - m);
+        const float4 v = *reinterpret_cast<const float4*>(a.part + slot * D + c * 4);
+        l = fmaf(w, ml.y, l);
+        o0 = fmaf(w, v.x, o0);
+        o1 = fmaf(w, v.y, o1);
+        o2 = fmaf(w, v.z, o2);
+        o3 = fmaf(w, v.w, o3);
     }
+    const float inv = 1.f / l;
+    bf16x4 q;
+    q[0] = static_cast<__bf16>(o0 * inv);
+    q[1] = static_cast<__bf16>(o1 * inv);
+    q[2] = static_cast<__bf16>(o2 * inv);
+    q[3] = static_cast<__bf16>(o3 * inv);
+    __bf16* Op = static_cast<__bf16*>(a.O) + size_t(bh) * size_t(T) * D;
+    *reinterpret_cast<bf16x4*>(Op + size_t(qi) * D + c * 4) = q;
+    if (a.lse && c == 0) a.lse[size_t(bh) * T + qi] = (m + __log2f(l)) * 0.6931471805599453f;
 }
 
 template <int D, int NG, int NW, bool SUB = false>
@@ -525,15 +531,18 @@ int fast_variant() {
 int launch_fwd_merge(int d, const FwdArgs& a, const int32_t* split_qb, const int32_t* split_ptr,
                      int32_t n_split, void* stream) {
     if (n_split <= 0 || a.sub != 1) return SA_ERR_UNSUPPORTED;
-    const dim3 grid(static_cast<unsigned>(int64_t(a.BH) * n_split));
-    if (d == 128)
-        hipLaunchKernelGGL(sa_fwd_merge_kernel<128>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a,
-                           split_qb, split_ptr, n_split);
-    else if (d == 64)
-        hipLaunchKernelGGL(sa_fwd_merge_kernel<64>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a,
-                           split_qb, split_ptr, n_split);
-    else
-        return SA_ERR_UNSUPPORTED;
+    auto go = [&](auto kernel, int rpw) {
+        if (a.bq % rpw) return SA_ERR_UNSUPPORTED;
+        const int64_t g = int64_t(a.BH) * n_split * (a.bq / rpw);
+        if (g > INT32_MAX) return SA_ERR_SHAPE;
+        hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(g)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                           a, split_qb, split_ptr, n_split);
+        return SA_OK;
+    };
+    int rc = d == 128 ? go(sa_fwd_merge_kernel<128>, MergeShape<128>::RPW)
+             : d == 64 ? go(sa_fwd_merge_kernel<64>, MergeShape<64>::RPW)
+                       : SA_ERR_UNSUPPORTED;
+    if (rc != SA_OK) return rc;
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
