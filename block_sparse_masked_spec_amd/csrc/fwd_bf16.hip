@@ -6,11 +6,12 @@
 // sliding-window attention", getnybble.com, "Implementation").  What differs
 // is how a tile is fed to the matrix cores:
 //
-//   * a workgroup of NW wavefronts covers 128 queries; each wave owns NG
-//     groups of 32 queries (one MFMA column block each).  With NG = 2 every
-//     K or V fragment read from LDS feeds two MFMAs; with NG = 1 a wave needs
-//     at most 256 registers, so two waves share each SIMD and one wave's
-//     softmax runs while the other's matrix products do;
+//   * a workgroup of NW wavefronts covers the query block (128 rows, or 64
+//     with two waves); each wave owns NG groups of 32 queries (one MFMA
+//     column block each).  The launches use NG = 1: a wave then needs at
+//     most 256 registers, so two waves share each SIMD and one wave's softmax
+//     can run while the other's matrix products do.  (NG = 2 would feed two
+//     MFMAs per fragment read but, at one wave per SIMD, measured slower);
 //   * LDS holds each K and V tile "fragment-major": for every MFMA k-step,
 //     the 64 lanes' operand pieces are stored contiguously in lane order.
 //     Every fragment read is then lane_base + a compile-time offset and 32
@@ -29,7 +30,6 @@
 //     PV MFMA consumes).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "internal.hpp"
 #include "kernel_common.hpp"
@@ -516,16 +516,6 @@ int launch_t(const FwdArgs& a, int64_t grid, void* stream) {
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
-// Which wave shape to use: SA_FAST_VARIANT=1 selects 64 queries per wave
-// (2 waves per workgroup), otherwise 32 queries per wave (4 waves).
-int fast_variant() {
-    static const int v = [] {
-        const char* e = getenv("SA_FAST_VARIANT");
-        return (e && e[0] == '1') ? 1 : 0;
-    }();
-    return v;
-}
-
 }  // namespace
 
 int launch_fwd_merge(int d, const FwdArgs& a, const int32_t* split_qb, const int32_t* split_ptr,
@@ -549,7 +539,6 @@ int launch_fwd_merge(int d, const FwdArgs& a, const int32_t* split_qb, const int
 // Returns SA_ERR_UNSUPPORTED when (dtype, d) has no fast path.
 int launch_fwd_fast(int dtype, int d, const FwdArgs& a, int64_t grid, void* stream) {
     if (dtype != SA_DTYPE_BF16) return SA_ERR_UNSUPPORTED;
-    const bool wide = fast_variant() == 1;
     if (a.sub > 1 && a.bq != kBQ) return SA_ERR_UNSUPPORTED;
     if (a.sub > 1) {  // interleaved subsequences: strided rows
         if (d == 128) return launch_t<128, 1, 4, true>(a, grid, stream);
@@ -557,8 +546,8 @@ int launch_fwd_fast(int dtype, int d, const FwdArgs& a, int64_t grid, void* stre
         return SA_ERR_UNSUPPORTED;
     }
     if (a.bq == 64) return d == 64 ? launch_t<64, 1, 2>(a, grid, stream) : SA_ERR_UNSUPPORTED;
-    if (d == 128) return wide ? launch_t<128, 2, 2>(a, grid, stream) : launch_t<128, 1, 4>(a, grid, stream);
-    if (d == 64) return wide ? launch_t<64, 2, 2>(a, grid, stream) : launch_t<64, 1, 4>(a, grid, stream);
+    if (d == 128) return launch_t<128, 1, 4>(a, grid, stream);
+    if (d == 64) return launch_t<64, 1, 4>(a, grid, stream);
     return SA_ERR_UNSUPPORTED;
 }
 
