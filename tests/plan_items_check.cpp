@@ -1,0 +1,172 @@
+// Host-side check of the forward plan's work items (built with g++ by
+// tests/test_plan_items.py; no GPU).  For random mask specs, lengths, tile
+// heights and split caps it builds the plan twice -- one item per query
+// block, and split -- and checks that the split items of each block, taken in
+// order, hold exactly the block's in-place tiles (with their mask flags) and
+// its gathered key list, that gathered cuts fall on whole tiles, that the
+// partial slots and the merge lists agree, and that the item order is a
+// permutation, heaviest first.  Prints "ok <cases>" and exits 0, or prints
+// the first mismatch and exits 1.
+#include <algorithm>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../block_sparse_masked_spec_amd/csrc/internal.hpp"
+
+namespace {
+
+struct Lcg {
+    uint64_t s;
+    uint32_t next() {
+        s = s * 6364136223846793005ull + 1442695040888963407ull;
+        return uint32_t(s >> 33);
+    }
+    int below(int n) { return int(next() % uint32_t(n)); }
+};
+
+std::string random_spec(Lcg& r, int T) {
+    std::string s;
+    const int mode = r.below(3);
+    if (mode == 2) {
+        const int blk = r.below(2) ? 64 : 32 * (1 + r.below(4));
+        s = "blocks;block=" + std::to_string(blk) + ";radius=" + std::to_string(r.below(3)) +
+            ";random=" + std::to_string(r.below(4)) + ";seed=" + std::to_string(r.below(100));
+    } else if (mode == 1) {
+        s = "bidir";
+        if (r.below(4)) s += ";radius=" + std::to_string(r.below(300));
+    } else {
+        s = "causal;window=" + std::to_string(r.below(5) ? 1 + r.below(400) : 0);
+        if (r.below(4) == 0) s += ";dilation=" + std::to_string(1 + r.below(3));
+    }
+    if (r.below(2)) {
+        const int st = 2 + r.below(40);
+        s += ";stride=" + std::to_string(st) + ";phase=" + std::to_string(r.below(st));
+    }
+    const int ng = r.below(3);
+    if (ng) {
+        s += ";global=";
+        for (int k = 0; k < ng; ++k) {
+            const int a = r.below(T), b = a + 1 + r.below(std::max(1, T / 8));
+            s += (k ? "," : "") + std::to_string(a) + ":" + std::to_string(std::min(b, T));
+        }
+    }
+    return s;
+}
+
+// The tiles of item `it` (or block `it` of an unsplit plan): in-place
+// (kb | flag) words, then its gathered key indices into colkeys.
+void expand(const sa::HostPlan& p, int it, std::vector<int32_t>& inplace, std::vector<int32_t>& keys) {
+    for (int r = p.run_ptr[it]; r < p.run_ptr[it + 1]; ++r) {
+        const int32_t kb0 = p.runs[2 * r], end = p.runs[2 * r + 1];
+        const int32_t flag = end & int32_t(0x80000000u);
+        for (int32_t kb = kb0; kb < (end & 0x7fffffff); ++kb) inplace.push_back(kb | flag);
+    }
+    const int32_t* g = &p.gseg[4 * size_t(it)];
+    for (int32_t x = g[0]; x < g[1]; ++x) keys.push_back(x);
+    for (int32_t x = g[2]; x < g[3]; ++x) keys.push_back(x);
+}
+
+int fail(const std::string& what, const std::string& spec, int T, int bq, int64_t cap) {
+    std::printf("mismatch: %s (spec %s, T=%d, bq=%d, cap=%lld)\n", what.c_str(), spec.c_str(), T, bq,
+                static_cast<long long>(cap));
+    return 1;
+}
+
+int check(const std::string& spec, int T, int bq, int64_t cap) {
+    sa_mask m;
+    if (sa::parse_mask_spec(spec.c_str(), &m) != SA_OK) return fail("spec does not parse", spec, T, bq, cap);
+    const sa::MaskRule rule(m, T);
+    const sa::HostPlan one = sa::build_plan(rule, bq, sa::kBK, 0);
+    const sa::HostPlan sp = sa::build_plan(rule, bq, sa::kBK, cap);
+    if (one.n_items != one.n_qb || one.n_parts != 0) return fail("unsplit plan has split items", spec, T, bq, cap);
+    if (sp.n_qb != one.n_qb || sp.inplace_tiles != one.inplace_tiles || sp.gathered_tiles != one.gathered_tiles)
+        return fail("totals differ", spec, T, bq, cap);
+    // The cap in force: automatic caps follow the mean block.
+    int64_t total = 0;
+    for (int qb = 0; qb < one.n_qb; ++qb) {
+        std::vector<int32_t> in, keys;
+        expand(one, qb, in, keys);
+        total += int64_t(in.size()) + int64_t((keys.size() + sa::kBK - 1) / sa::kBK);
+    }
+    const int64_t mean = (total + one.n_qb - 1) / one.n_qb;
+    const int64_t eff = cap == sa::kSplitAuto ? std::max<int64_t>(sa::kSplitMinTiles, 2 * mean) : cap;
+    // Items of each block, in index order.
+    int it = 0, parts = 0;
+    std::vector<int64_t> work(sp.n_items, 0);
+    for (int qb = 0; qb < one.n_qb; ++qb) {
+        std::vector<int32_t> want_in, want_keys, got_in, got_keys;
+        expand(one, qb, want_in, want_keys);
+        const int first = it;
+        while (it < sp.n_items && sp.item_qb[it] == qb) {
+            const size_t before = got_keys.size();
+            const size_t in_before = got_in.size();
+            expand(sp, it, got_in, got_keys);
+            const size_t nk = got_keys.size() - before;
+            work[it] = int64_t(got_in.size() - in_before) + int64_t((nk + sa::kBK - 1) / sa::kBK);
+            if (work[it] < 1) return fail("empty item", spec, T, bq, cap);
+            // a cut inside the gathered list must fall on a whole tile
+            const bool more_keys_follow = got_keys.size() < want_keys.size();
+            if (more_keys_follow && nk % sa::kBK) return fail("gathered cut inside a tile", spec, T, bq, cap);
+            ++it;
+        }
+        const int n = it - first;
+        if (n == 0) return fail("block without items", spec, T, bq, cap);
+        if (got_in != want_in) return fail("in-place tiles differ", spec, T, bq, cap);
+        if (got_keys != want_keys) return fail("gathered keys differ", spec, T, bq, cap);
+        const int64_t w = int64_t(want_in.size()) + int64_t((want_keys.size() + sa::kBK - 1) / sa::kBK);
+        const int64_t expect = w > eff ? (w + eff - 1) / eff : 1;
+        if (n != expect) return fail("item count", spec, T, bq, cap);
+        for (int x = first; x < it; ++x) {
+            const int32_t want = n > 1 ? parts + (x - first) : -1;
+            if (sp.item_part[x] != want) return fail("partial slot", spec, T, bq, cap);
+        }
+        if (n > 1) {
+            size_t s = 0;
+            while (s < sp.split_qb.size() && sp.split_qb[s] != qb) ++s;
+            if (s == sp.split_qb.size() || sp.split_ptr[s] != parts || sp.split_ptr[s + 1] != parts + n)
+                return fail("merge list", spec, T, bq, cap);
+            parts += n;
+        }
+    }
+    if (it != sp.n_items || parts != sp.n_parts) return fail("item or part count", spec, T, bq, cap);
+    std::vector<char> seen(sp.n_items, 0);
+    for (int x = 0; x < sp.n_items; ++x) {
+        const int32_t o = sp.qb_order[x];
+        if (o < 0 || o >= sp.n_items || seen[o]) return fail("order is not a permutation", spec, T, bq, cap);
+        seen[o] = 1;
+        if (x > 0 && work[sp.qb_order[x - 1]] < work[o]) return fail("order not heaviest first", spec, T, bq, cap);
+    }
+    return 0;
+}
+
+}  // namespace
+
+int main() {
+    Lcg r{12345};
+    int cases = 0;
+    // fixed cases: the Longformer 16K layer and a global block mid-sequence
+    const struct {
+        const char* spec;
+        int T, bq;
+    } fixed[] = {{"bidir;radius=256;stride=16;phase=0;global=0:128", 16384, 128},
+                 {"causal;window=64;global=3000:3050", 5000, 128},
+                 {"blocks;block=64;radius=1;random=3;seed=0;global=0:128", 4096, 64}};
+    for (const auto& f : fixed)
+        for (int64_t cap : {int64_t(sa::kSplitAuto), int64_t(1), int64_t(7), int64_t(60)}) {
+            if (check(f.spec, f.T, f.bq, cap)) return 1;
+            ++cases;
+        }
+    for (int n = 0; n < 400; ++n) {
+        const int T = 1 + r.below(n < 200 ? 700 : 3000);
+        const std::string spec = random_spec(r, T);
+        const int bq = r.below(2) ? 128 : 64;
+        const int64_t caps[] = {sa::kSplitAuto, 1, 2, 3, 5, 16};
+        const int64_t cap = caps[r.below(6)];
+        if (check(spec, T, bq, cap)) return 1;
+        ++cases;
+    }
+    std::printf("ok %d\n", cases);
+    return 0;
+}

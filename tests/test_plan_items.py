@@ -1,0 +1,31 @@
+"""Host-side check of the forward plan's work items (no GPU).
+
+Builds tests/plan_items_check.cpp with the library's host planner sources
+(plan.cpp, mask_spec.cpp) using g++, and runs it: for fixed and random mask
+specs, lengths, tile heights and split caps, the items of each query block,
+taken in order, must hold exactly the block's in-place tiles and gathered
+keys, cut on whole tiles, with consistent partial slots, merge lists and a
+heaviest-first order.  The split is a rearrangement of work, so the fp64
+oracle is not involved; the GPU parity tests then check the merged results.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "..", "block_sparse_masked_spec_amd", "csrc")
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_split_items_cover_each_block_exactly(tmp_path):
+    exe = str(tmp_path / "plan_items_check")
+    build = subprocess.run(
+        ["g++", "-std=c++20", "-O1", "-Wall", "-o", exe, os.path.join(HERE, "plan_items_check.cpp"),
+         os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "mask_spec.cpp")],
+        capture_output=True, text=True, timeout=300)
+    assert build.returncode == 0, build.stderr[-2000:]
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert run.returncode == 0 and run.stdout.startswith("ok"), run.stdout[-2000:] + run.stderr[-2000:]
+    assert int(run.stdout.split()[1]) >= 400
