@@ -41,6 +41,9 @@ int parse_for(const char* spec, int T, sa_mask* m) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Largest workspace the split partials may take.
+constexpr size_t kMaxSplitWorkspace = size_t(1) << 30;
+
 // Tile cap of the fast path's work items: automatic, or SA_FWD_SPLIT_TILES=n
 // (n > 0) to split every query block above n tiles.
 int64_t split_cap() {
@@ -296,6 +299,13 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     DevicePlan dp;
     rc = cache().get(m, Ts, bq, fast && sub == 1 ? split_cap() : 0, &dp);
     if (rc != SA_OK) return rc;
+    // Partial slots grow with B*H: past kMaxSplitWorkspace the unsplit plan
+    // runs instead (slower on blocks of global rows, same result).
+    const size_t pbytes = size_t(BH) * size_t(dp.n_parts) * bq * (size_t(d) + 2) * sizeof(float);
+    if (dp.n_parts > 0 && pbytes > kMaxSplitWorkspace) {
+        rc = cache().get(m, Ts, bq, 0, &dp);
+        if (rc != SA_OK) return rc;
+    }
     if (BH * sub * int64_t(dp.n_items) > INT32_MAX) return SA_ERR_SHAPE;
     sa::FwdArgs a;
     a.Q = Q;
@@ -331,7 +341,6 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     a.part = nullptr;
     a.n_parts = dp.n_parts;
     if (dp.n_parts > 0) {
-        const size_t pbytes = size_t(a.BH) * dp.n_parts * bq * (size_t(d) + 2) * sizeof(float);
         rc = workspace().get(pbytes, stream, &a.part);
         if (rc != SA_OK) return rc;
     }

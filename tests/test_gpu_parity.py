@@ -271,6 +271,22 @@ def test_split_blocks_forced(gpu, monkeypatch, spec, T, d, cap):
     lse_check(gpu, spec, 2, 3, T, d, seed=cap)
 
 
+def test_split_workspace_limit_falls_back(gpu, monkeypatch):
+    """With every block split into one-tile items, 512 sequences would need
+    512 x 63 parts x 128 rows x 66 floats (1.09 GB) of partials, above the
+    1 GiB limit: the call runs the unsplit plan instead.  Four heads checked
+    in full against the oracle."""
+    spec, B, H, T, d = "bidir;radius=64;stride=16;phase=0;global=0:128", 8, 64, 1000, 64
+    monkeypatch.setenv("SA_FWD_SPLIT_TILES", "1")
+    assert gpu.sparse_attn_plan_info(spec, T, d)["split_parts"] == 63
+    q, k, v = inputs.qkv(B, H, T, d, "bf16", 9)
+    got = run_gpu(gpu, spec, q, k, v)
+    for b, h in [(0, 0), (3, 17), (5, 40), (7, 63)]:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref, _, _ = oracle.forward_rows(spec, q[sl], k[sl], v[sl])
+        check_bf16(got[sl], ref, f"{spec} b={b} h={h}")
+
+
 def test_split_blocks_automatic(gpu):
     """Global rows in the middle of a causal window: their block (rows
     2944..3071) reads keys 0..3071, 48 tiles, against about 3 for the rest,
