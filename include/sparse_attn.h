@@ -65,7 +65,16 @@
  * Ownership.  The caller owns Q, K, V and O; the library never allocates,
  * frees or keeps them.  The library owns a per-device cache of execution
  * plans (tile lists for one spec and T), built on first use and freed by
- * sparse_attn_release_cache().  Calls are thread-safe.
+ * sparse_attn_release_cache(), and an fp32 workspace per (device, stream),
+ * grown on demand: the bf16 forward's partial results when a plan splits
+ * a heavy query block (at most 1 GiB; past that the unsplit plan runs), the
+ * backward's row dots and decode's key-split partials.  Calls are
+ * thread-safe; calls that share a stream use its workspace in stream order.
+ *
+ * Tuning.  SA_FWD_SPLIT_TILES=n (n > 0) in the environment makes the bf16
+ * forward split every query block above n key tiles into work items (the
+ * default splits blocks above max(16, twice the mean)); the result is the
+ * same up to rounding order.
  *
  * Streams.  Device work is enqueued on `stream` (a hipStream_t; NULL = the
  * null stream) of the current device; the call returns after the enqueue.
@@ -281,7 +290,7 @@ int sparse_attn_decode_cache_rows(const char* mask_spec, int n_new, int64_t* row
 /* Static text for a status code. */
 const char* sparse_attn_strerror(int status);
 
-/* Free every cached plan and decode workspace on every device.  The caller
+/* Free every cached plan and workspace on every device.  The caller
  * must make sure no launched kernel still uses them (synchronise first). */
 void sparse_attn_release_cache(void);
 
