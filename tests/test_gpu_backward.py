@@ -26,6 +26,7 @@ import torch
 
 import oracle
 from block_sparse_masked_spec_amd import inputs
+from spec_fuzz import random_spec
 
 pytestmark = pytest.mark.gpu
 
@@ -124,6 +125,23 @@ def test_backward_block_mode_64_row_tiles(gpu, T):
     for spec in specs:
         assert gpu.sparse_attn_plan_info(spec, T, 64)["bq"] == 64
         full_check(gpu, spec, 2, 2, T, 64, "bf16", seed=T)
+
+@pytest.mark.parametrize("case", range(80))
+def test_backward_random_specs(gpu, case):
+    """Seeded random specs (all modes and fields, ragged lengths up to 600):
+    forward LSE and dQ, dK, dV against the oracle, bf16 d = 64 / 128 on the
+    fast kernels and fp32 or small d on the generic ones."""
+    import random
+    rng = random.Random(5000 + case)
+    T = rng.randrange(1, 600)
+    spec = random_spec(rng, T)
+    B, H = rng.randrange(1, 3), rng.randrange(1, 3)
+    if case % 4 == 3:
+        d, dtype = rng.choice([16, 32, 64]), "f32"
+    else:
+        d, dtype = rng.choice([64, 128]), "bf16"
+    full_check(gpu, spec, B, H, T, d, dtype, seed=case)
+
 
 def test_backward_window_layer_2k(gpu):
     """B=1, H=4, T=2048, d=128, causal window 256: every gradient compared."""

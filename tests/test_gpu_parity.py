@@ -15,6 +15,7 @@ import torch
 
 import oracle
 from block_sparse_masked_spec_amd import inputs
+from spec_fuzz import random_spec
 
 pytestmark = pytest.mark.gpu
 
@@ -269,6 +270,26 @@ def test_split_blocks_forced(gpu, monkeypatch, spec, T, d, cap):
     info = gpu.sparse_attn_plan_info(spec, T, d)
     assert info["split_parts"] > 0
     lse_check(gpu, spec, 2, 3, T, d, seed=cap)
+
+
+@pytest.mark.parametrize("case", range(160))
+def test_random_specs(gpu, monkeypatch, case):
+    """Seeded random specs (all modes and fields, ragged lengths up to 900),
+    on the bf16 fast path with and without forced splits (O and LSE), and on
+    the generic path (fp32, small d), against the oracle."""
+    import random
+    rng = random.Random(1000 + case)
+    T = rng.randrange(1, 900)
+    spec = random_spec(rng, T)
+    B, H = rng.randrange(1, 3), rng.randrange(1, 4)
+    if case % 4 == 3:
+        d, dtype = rng.choice([16, 32, 64]), rng.choice(["f32", "bf16"] if case % 8 == 3 else ["f32"])
+        full_check(gpu, spec, B, H, T, d, dtype, seed=case)
+        return
+    cap = rng.choice([None, None, 1, 2, 5])
+    if cap:
+        monkeypatch.setenv("SA_FWD_SPLIT_TILES", str(cap))
+    lse_check(gpu, spec, B, H, T, rng.choice([64, 128]), seed=case)
 
 
 def test_split_workspace_limit_falls_back(gpu, monkeypatch):

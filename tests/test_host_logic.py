@@ -239,6 +239,25 @@ def test_plan_window_overhead():
     assert info["executed_cells"] / info["allowed_cells"] < 1.05
 
 
+@pytest.mark.parametrize("chunk", range(4))
+def test_random_specs_counts_and_tile_maps(chunk):
+    """Seeded random specs (the GPU fuzz generator), 50 per chunk: allowed
+    cells, per-row counts and the tile map at the forward's tile shape,
+    bit-exact against the oracle."""
+    import random
+    from spec_fuzz import random_spec
+    for case in range(50 * chunk, 50 * chunk + 50):
+        rng = random.Random(9000 + case)
+        T = rng.randrange(1, 700)
+        spec = random_spec(rng, T)
+        total, rows = sa.sparse_attn_count(spec, T, row_counts=True)
+        ref_total, ref_rows = oracle.count(spec, T, per_row=True)
+        assert total == ref_total, spec
+        assert np.array_equal(rows.astype(np.int64), ref_rows), spec
+        bq, bk = sa.sparse_attn_tile_shape(64)
+        assert np.array_equal(sa.sparse_attn_tile_map(spec, T, bq, bk), oracle.tile_map(spec, T, bq, bk)), spec
+
+
 def test_plan_splits_blocks_of_global_rows(monkeypatch):
     """Longformer 16K at d = 64: the block of global rows 0..127 reads all 256
     key tiles, the mean block ceil(3800 / 128) = 30, so the fast path's plan
