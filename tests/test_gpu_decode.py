@@ -132,6 +132,31 @@ def test_mistral_decode_batch_sampled(gpu):
                check_rows=[0, 1, 2, 17, 40, 63])
 
 
+@pytest.mark.parametrize("case", range(40))
+def test_decode_random_shapes(gpu, case):
+    """Seeded random decode calls: window (or unlimited, then every position
+    still cached), dilation, head grouping, new-token count, head size,
+    cache length at or above the minimum, and per-sequence positions before
+    and long after the ring wraps."""
+    import random
+    rng = random.Random(7000 + case)
+    d = rng.choice([16, 32, 64, 128])
+    H, Hkv = rng.choice([(1, 1), (4, 1), (8, 2), (6, 3), (16, 4), (32, 8)])
+    n_new = rng.choice([1, 1, 1, 2, 3, 5])
+    dil = rng.choice([1, 1, 2, 3])
+    B = rng.randrange(1, 5)
+    if rng.random() < 0.15:
+        spec = "causal;window=0" + (f";dilation={dil}" if dil > 1 else "")
+        C = rng.randrange(n_new, 1500)
+        hi = C  # unlimited window: the cache holds the whole context
+    else:
+        spec = f"causal;window={rng.randrange(1, 800)}" + (f";dilation={dil}" if dil > 1 else "")
+        C = gpu.sparse_attn_decode_cache_rows(spec, n_new) + rng.randrange(0, 300)
+        hi = C + 3000
+    pos = [rng.randrange(n_new - 1, hi) for _ in range(B)]
+    run_decode(gpu, spec, B, H, Hkv, n_new, C, d, pos, seed=case)
+
+
 def test_decode_matches_forward_last_rows(gpu):
     """Decode of the last token equals the forward's last row computed by the
     library's own forward kernel on the same inputs (MHA, full sequence)."""
