@@ -27,7 +27,11 @@
 //     (log2 domain), so the accumulator rescale is almost never paid --
 //     exact either way, since every weight of a row uses the same reference;
 //   * row sums add the bf16-rounded weights with v_dot2 (the same values the
-//     PV MFMA consumes).
+//     PV MFMA consumes);
+//   * a workgroup runs one work item of the plan: a query block, or one
+//     key range of a block far heavier than the mean (a block of global
+//     rows), whose unnormalised result a merge kernel combines with the
+//     block's other ranges.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
