@@ -125,20 +125,24 @@ class PlanCache {
     }
 
     // The backward plan (key blocks -> query tiles) for (spec, T).
-    int get_bwd(const sa_mask& m, int T, int bkb, sa::BwdDevicePlan* out) {
+    int get_bwd(const sa_mask& m, int T, int bkb, int64_t split_cap, sa::BwdDevicePlan* out) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return SA_ERR_HIP;
         std::string key = sa::canonical_spec(m) + "|T=" + std::to_string(T) + "|bwd|bkb=" +
-                          std::to_string(bkb) + "|dev=" + std::to_string(dev);
+                          std::to_string(bkb) + "|split=" + std::to_string(split_cap) +
+                          "|dev=" + std::to_string(dev);
         std::lock_guard<std::mutex> lock(mu_);
         auto it = bwd_.find(key);
         if (it != bwd_.end()) {
             *out = it->second.plan;
             return SA_OK;
         }
-        sa::BwdHostPlan hp = sa::build_bwd_plan(MaskRule(m, T), bkb);
+        sa::BwdHostPlan hp = sa::build_bwd_plan(MaskRule(m, T), bkb, split_cap);
         sa::BwdDevicePlan dp;
         dp.n_kb = hp.n_kb;
+        dp.n_items = hp.n_items;
+        dp.n_parts = hp.n_parts;
+        dp.n_split = static_cast<int32_t>(hp.split_kb.size());
         size_t off = 0;
         auto section = [&](size_t bytes, size_t* where) {
             off = align_up(off, 16);
@@ -148,6 +152,10 @@ class PlanCache {
         section(hp.kb_order.size() * 4, &dp.off_order);
         section(hp.kb_ptr.size() * 4, &dp.off_ptr);
         section(hp.kb_runs.size() * 4, &dp.off_runs);
+        section(hp.item_kb.size() * 4, &dp.off_item_kb);
+        section(hp.item_part.size() * 4, &dp.off_item_part);
+        section(hp.split_kb.size() * 4, &dp.off_split_kb);
+        section(hp.split_ptr.size() * 4, &dp.off_split_ptr);
         dp.bytes = align_up(off, 16) + 16;
         std::vector<unsigned char> host(dp.bytes, 0);
         auto put = [&](size_t where, const void* src, size_t bytes) {
@@ -156,6 +164,10 @@ class PlanCache {
         put(dp.off_order, hp.kb_order.data(), hp.kb_order.size() * 4);
         put(dp.off_ptr, hp.kb_ptr.data(), hp.kb_ptr.size() * 4);
         put(dp.off_runs, hp.kb_runs.data(), hp.kb_runs.size() * 4);
+        put(dp.off_item_kb, hp.item_kb.data(), hp.item_kb.size() * 4);
+        put(dp.off_item_part, hp.item_part.data(), hp.item_part.size() * 4);
+        put(dp.off_split_kb, hp.split_kb.data(), hp.split_kb.size() * 4);
+        put(dp.off_split_ptr, hp.split_ptr.data(), hp.split_ptr.size() * 4);
         if (hipMalloc(&dp.base, dp.bytes) != hipSuccess) {
             (void)hipGetLastError();
             return SA_ERR_NOMEM;
@@ -387,14 +399,37 @@ int backward(int dtype, const void* Q, const void* K, const void* V, const void*
     // the backward uses 64-query blocks and 64-key blocks as well.
     const int bq = sa::fwd_query_block(m, d, dtype);
     const int bkb = bq == 64 ? 64 : sa::kBKB;
+    // The bf16 d = 64 / 128 kernels run split plans (heavy query blocks and
+    // heavy key blocks as several items); the generic kernels do not.
+    const bool dma = dtype == SA_DTYPE_BF16 && (d == 64 || d == 128);
+    const int64_t cap = dma ? split_cap() : 0;
     DevicePlan dp;
-    rc = cache().get(m, T, bq, 0, &dp);
+    rc = cache().get(m, T, bq, cap, &dp);
     if (rc != SA_OK) return rc;
     sa::BwdDevicePlan bp;
-    rc = cache().get_bwd(m, T, bkb, &bp);
+    rc = cache().get_bwd(m, T, bkb, cap, &bp);
     if (rc != SA_OK) return rc;
+    // Workspace: row dots D_i, then dQ partials, then dK and dV partials
+    // (each section 256-byte aligned).  Past kMaxSplitWorkspace of partials
+    // the unsplit plans run instead.
+    auto sized = [&](const DevicePlan& f, const sa::BwdDevicePlan& k, size_t* q_off, size_t* kv_off) {
+        size_t off = align_up(lbytes, 256);
+        *q_off = off;
+        off += align_up(size_t(BH) * size_t(f.n_parts) * bq * size_t(d) * sizeof(float), 256);
+        *kv_off = off;
+        off += 2 * size_t(BH) * size_t(k.n_parts) * bkb * size_t(d) * sizeof(float);
+        return off;
+    };
+    size_t q_off = 0, kv_off = 0;
+    size_t wbytes = sized(dp, bp, &q_off, &kv_off);
+    if (wbytes - align_up(lbytes, 256) > kMaxSplitWorkspace) {
+        rc = cache().get(m, T, bq, 0, &dp);
+        if (rc == SA_OK) rc = cache().get_bwd(m, T, bkb, 0, &bp);
+        if (rc != SA_OK) return rc;
+        wbytes = sized(dp, bp, &q_off, &kv_off);
+    }
     float* Dw = nullptr;
-    rc = workspace().get(lbytes, stream, &Dw);
+    rc = workspace().get(wbytes, stream, &Dw);
     if (rc != SA_OK) return rc;
 
     sa::BwdArgs b;
@@ -426,10 +461,10 @@ int backward(int dtype, const void* Q, const void* K, const void* V, const void*
     a.blk_iv = reinterpret_cast<const int32_t*>(base + dp.off_blk_iv);
     a.lse = nullptr;
     a.bq = bq;
-    a.item_qb = nullptr;
-    a.item_part = nullptr;
+    a.item_qb = reinterpret_cast<const int32_t*>(base + dp.off_item_qb);
+    a.item_part = dp.n_parts > 0 ? reinterpret_cast<const int32_t*>(base + dp.off_item_part) : nullptr;
     a.part = nullptr;
-    a.n_parts = 0;
+    a.n_parts = dp.n_parts;
     b.dO = dO;
     b.lse = lse;
     b.dQ = dQ;
@@ -442,6 +477,21 @@ int backward(int dtype, const void* Q, const void* K, const void* V, const void*
     b.kb_ptr = reinterpret_cast<const int32_t*>(bb + bp.off_ptr);
     b.kb_runs = reinterpret_cast<const int32_t*>(bb + bp.off_runs);
     b.n_kb = bp.n_kb;
+    b.n_q_items = dp.n_items;
+    b.n_kv_items = bp.n_items;
+    auto* wb = reinterpret_cast<unsigned char*>(Dw);
+    b.dq_part = dp.n_parts > 0 ? reinterpret_cast<float*>(wb + q_off) : nullptr;
+    b.dq_split_qb = reinterpret_cast<const int32_t*>(base + dp.off_split_qb);
+    b.dq_split_ptr = reinterpret_cast<const int32_t*>(base + dp.off_split_ptr);
+    b.dq_n_split = dp.n_split;
+    b.kv_item_kb = reinterpret_cast<const int32_t*>(bb + bp.off_item_kb);
+    b.kv_item_part = bp.n_parts > 0 ? reinterpret_cast<const int32_t*>(bb + bp.off_item_part) : nullptr;
+    b.kv_part = bp.n_parts > 0 ? reinterpret_cast<float*>(wb + kv_off) : nullptr;
+    b.kv_split_kb = reinterpret_cast<const int32_t*>(bb + bp.off_split_kb);
+    b.kv_split_ptr = reinterpret_cast<const int32_t*>(bb + bp.off_split_ptr);
+    b.kv_n_split = bp.n_split;
+    b.kv_n_parts = bp.n_parts;
+    if (BH * int64_t(std::max(dp.n_items, bp.n_items)) > INT32_MAX) return SA_ERR_SHAPE;
     return sa::launch_bwd(dtype, d, b, stream);
 }
 

@@ -130,6 +130,23 @@ __device__ __forceinline__ void store_rows(E* dst, const f32x16* acc, int row, i
         }
 }
 
+// Row `row` of a [rows][D] fp32 block, same element mapping as store_rows
+// (a partial result of a split work item, unscaled).
+template <int D>
+__device__ __forceinline__ void store_rows_f32(float* dst, const f32x16* acc, int row, int h) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float4 q;
+            q.x = acc[db][g * 4];
+            q.y = acc[db][g * 4 + 1];
+            q.z = acc[db][g * 4 + 2];
+            q.w = acc[db][g * 4 + 3];
+            *reinterpret_cast<float4*>(dst + size_t(row) * D + db * 32 + g * 8 + h * 4) = q;
+        }
+}
+
 // ---------------------------------------------------------------- dQ kernel
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void sa_bwd_dq_kernel(BwdArgs b) {
@@ -533,9 +550,10 @@ __global__ __launch_bounds__(NW * 64, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, h = lane >> 5;
     const int work = xcd_slice_index(blockIdx.x, gridDim.x);
-    const int n_qb = gridDim.x / a.BH;
-    const int bh = work / n_qb;
-    const int qb = ldc(a.qb_order, work % n_qb);
+    const int n_items = gridDim.x / a.BH;
+    const int bh = work / n_items;
+    const int it = ldc(a.qb_order, work % n_items);  // a query block or one key range of it
+    const int qb = ldc(a.item_qb, it);
     const int T = a.T;
     const size_t base = size_t(bh) * size_t(T) * D;
     const E* Qp = static_cast<const E*>(a.Q) + base;
@@ -565,8 +583,8 @@ __global__ __launch_bounds__(NW * 64, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
 #pragma unroll
     for (int db = 0; db < S::NDB; ++db) acc[db] = f32x16{};
 
-    const int ga0 = ldc(a.gseg, 4 * qb), ga1 = ldc(a.gseg, 4 * qb + 1);
-    const int gb0 = ldc(a.gseg, 4 * qb + 2), gb1 = ldc(a.gseg, 4 * qb + 3);
+    const int ga0 = ldc(a.gseg, 4 * it), ga1 = ldc(a.gseg, 4 * it + 1);
+    const int gb0 = ldc(a.gseg, 4 * it + 2), gb1 = ldc(a.gseg, 4 * it + 3);
     const int gna = ga1 - ga0, gtot = gna + (gb1 - gb0);
     auto gkey = [&](int slot) { return a.colkeys[slot < gna ? ga0 + slot : gb0 + (slot - gna)]; };
 
@@ -605,7 +623,7 @@ __global__ __launch_bounds__(NW * 64, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
     };
 
     // Tile t computes from slot t % 2 while tile t + 1 loads into the other.
-    BwdCursor cur{ldc(a.run_ptr, qb), ldc(a.run_ptr, qb + 1), 0, 0, false, 0, gtot};
+    BwdCursor cur{ldc(a.run_ptr, it), ldc(a.run_ptr, it + 1), 0, 0, false, 0, gtot};
     bcur_enter(cur, a);
     int slot = 0;
     if (!cur.done()) issue(cur, kbuf, vbuf);
@@ -619,7 +637,12 @@ __global__ __launch_bounds__(NW * 64, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
         cur = nxt;
         slot ^= 1;
     }
-    if (qi < T) store_rows<E, D>(static_cast<E*>(b.dQ) + base, acc, qi, h, b.scale);
+    const int part = a.item_part ? ldc(a.item_part, it) : -1;
+    if (part >= 0)  // one key range of a split block: unscaled partial
+        store_rows_f32<D>(b.dq_part + (size_t(bh) * a.n_parts + part) * (NW * 32) * D, acc,
+                          qi - qb * (NW * 32), h);
+    else if (qi < T)
+        store_rows<E, D>(static_cast<E*>(b.dQ) + base, acc, qi, h, b.scale);
 }
 
 template <int D, int NW>
@@ -640,8 +663,10 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kerne
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, h = lane >> 5;
     const int work = xcd_slice_index(blockIdx.x, gridDim.x);
-    const int bh = work / b.n_kb;
-    const int kb = ldc(b.kb_order, work % b.n_kb);
+    const int n_items = gridDim.x / a.BH;
+    const int bh = work / n_items;
+    const int it = ldc(b.kb_order, work % n_items);  // a key block or one query range of it
+    const int kb = ldc(b.kv_item_kb, it);
     const int T = a.T;
     const size_t base = size_t(bh) * size_t(T) * D;
     const E* Qp = static_cast<const E*>(a.Q) + base;
@@ -661,9 +686,9 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kerne
 #pragma unroll
     for (int db = 0; db < S::NDB; ++db) dk[db] = dv[db] = f32x16{};
 
-    // Query tiles of this key block: run r, tile qt.
-    int r = ldc(b.kb_ptr, kb);
-    const int r_end = ldc(b.kb_ptr, kb + 1);
+    // Query tiles of this item: run r, tile qt.
+    int r = ldc(b.kb_ptr, it);
+    const int r_end = ldc(b.kb_ptr, it + 1);
     int qt = 0, qt_end = 0;
     bool masked = false;
     auto enter = [&]() {
@@ -793,10 +818,48 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kerne
         cq = nq;
         cm = nm;
     }
-    if (kj < T) {
+    const int part = b.kv_item_part ? ldc(b.kv_item_part, it) : -1;
+    if (part >= 0) {  // one query range of a split key block: unscaled partials
+        const size_t slot = (size_t(bh) * b.kv_n_parts + part) * (NW * 32) * D;
+        const size_t half = size_t(a.BH) * b.kv_n_parts * (NW * 32) * D;
+        store_rows_f32<D>(b.kv_part + slot, dk, kj - kb * (NW * 32), h);
+        store_rows_f32<D>(b.kv_part + half + slot, dv, kj - kb * (NW * 32), h);
+    } else if (kj < T) {
         store_rows<E, D>(static_cast<E*>(b.dK) + base, dk, kj, h, b.scale);
         store_rows<E, D>(static_cast<E*>(b.dV) + base, dv, kj, h, 1.f);
     }
+}
+
+// Sum the partials of the split blocks into the bf16 output: rows of block
+// split_blk[s] get mul * the sum over slots [split_ptr[s], split_ptr[s+1])
+// of part[bh][slot][row][:].  One thread per (row, 4 columns).
+template <int D>
+__global__ __launch_bounds__(256) void sa_bwd_sum_parts_kernel(const float* part, int n_parts, int rows,
+                                                                const int32_t* split_blk,
+                                                                const int32_t* split_ptr, int n_split,
+                                                                __bf16* dst, int T, float mul) {
+    constexpr int C = D / 4, RPW = 256 / C;
+    const int per_blk = rows / RPW;
+    const int x = blockIdx.x % per_blk, y = blockIdx.x / per_blk;
+    const int bh = y / n_split, sidx = y % n_split;
+    const int r = x * RPW + threadIdx.x / C, c = threadIdx.x % C;
+    const int row = split_blk[sidx] * rows + r;
+    if (row >= T) return;
+    float4 sum = {0.f, 0.f, 0.f, 0.f};
+    for (int p = split_ptr[sidx]; p < split_ptr[sidx + 1]; ++p) {
+        const float4 v =
+            *reinterpret_cast<const float4*>(part + ((size_t(bh) * n_parts + p) * rows + r) * D + c * 4);
+        sum.x += v.x;
+        sum.y += v.y;
+        sum.z += v.z;
+        sum.w += v.w;
+    }
+    typename Ops<__bf16>::quad q;
+    q[0] = static_cast<__bf16>(sum.x * mul);
+    q[1] = static_cast<__bf16>(sum.y * mul);
+    q[2] = static_cast<__bf16>(sum.z * mul);
+    q[3] = static_cast<__bf16>(sum.w * mul);
+    *reinterpret_cast<typename Ops<__bf16>::quad*>(dst + (size_t(bh) * T + row) * D + c * 4) = q;
 }
 
 template <typename E, int D>
@@ -815,14 +878,34 @@ int launch_b(const BwdArgs& b, void* stream) {
 // plans of block mode).
 template <int D, int NW>
 int launch_b_dma(const BwdArgs& b, void* stream) {
-    const unsigned g1 = static_cast<unsigned>(int64_t(b.f.BH) * ((b.f.T + NW * 32 - 1) / (NW * 32)));
-    hipLaunchKernelGGL((sa_bwd_dq_dma_kernel<D, NW>), dim3(g1), dim3(NW * 64), 0,
-                       static_cast<hipStream_t>(stream), b);
+    constexpr int ROWS = NW * 32;  // query rows of a dQ block, keys of a dK/dV block
+    const auto st = static_cast<hipStream_t>(stream);
+    auto sum_parts = [&](const float* part, int n_parts, const int32_t* blk, const int32_t* ptr, int n_split,
+                         void* dst, float mul) {
+        const int64_t g = int64_t(b.f.BH) * n_split * (ROWS / (256 / (D / 4)));
+        if (g > INT32_MAX) return SA_ERR_SHAPE;
+        hipLaunchKernelGGL((sa_bwd_sum_parts_kernel<D>), dim3(static_cast<unsigned>(g)), dim3(256), 0, st, part,
+                           n_parts, ROWS, blk, ptr, n_split, static_cast<__bf16*>(dst), b.f.T, mul);
+        return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+    };
+    const unsigned g1 = static_cast<unsigned>(int64_t(b.f.BH) * b.n_q_items);
+    hipLaunchKernelGGL((sa_bwd_dq_dma_kernel<D, NW>), dim3(g1), dim3(NW * 64), 0, st, b);
     if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
-    const unsigned g2 = static_cast<unsigned>(int64_t(b.f.BH) * b.n_kb);
-    hipLaunchKernelGGL((sa_bwd_dkv_dma_kernel<D, NW>), dim3(g2), dim3(NW * 64), 0,
-                       static_cast<hipStream_t>(stream), b);
-    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+    if (b.f.n_parts > 0) {
+        const int rc = sum_parts(b.dq_part, b.f.n_parts, b.dq_split_qb, b.dq_split_ptr, b.dq_n_split, b.dQ, b.scale);
+        if (rc != SA_OK) return rc;
+    }
+    const unsigned g2 = static_cast<unsigned>(int64_t(b.f.BH) * b.n_kv_items);
+    hipLaunchKernelGGL((sa_bwd_dkv_dma_kernel<D, NW>), dim3(g2), dim3(NW * 64), 0, st, b);
+    if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
+    if (b.kv_n_parts > 0) {
+        const size_t half = size_t(b.f.BH) * b.kv_n_parts * ROWS * D;
+        int rc = sum_parts(b.kv_part, b.kv_n_parts, b.kv_split_kb, b.kv_split_ptr, b.kv_n_split, b.dK, b.scale);
+        if (rc == SA_OK)
+            rc = sum_parts(b.kv_part + half, b.kv_n_parts, b.kv_split_kb, b.kv_split_ptr, b.kv_n_split, b.dV, 1.f);
+        if (rc != SA_OK) return rc;
+    }
+    return SA_OK;
 }
 
 }  // namespace

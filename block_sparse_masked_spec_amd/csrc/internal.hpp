@@ -137,8 +137,9 @@ struct DevicePlan {
 struct BwdDevicePlan {
     void* base = nullptr;
     size_t bytes = 0;
-    int32_t n_kb = 0;
-    size_t off_order = 0, off_ptr = 0, off_runs = 0;
+    int32_t n_kb = 0, n_items = 0, n_parts = 0, n_split = 0;
+    size_t off_order = 0, off_ptr = 0, off_runs = 0, off_item_kb = 0, off_item_part = 0,
+           off_split_kb = 0, off_split_ptr = 0;
 };
 
 // Kernel arguments (passed by value).
@@ -190,16 +191,25 @@ constexpr int kBK = 64;
 constexpr int kBKB = 128;  // keys per dK/dV workgroup
 constexpr int kBQB = 64;   // queries per tile it visits
 
+// Work items as in HostPlan: a key block, or one range of the query tiles
+// of a key block far heavier than the mean (the key block of a global
+// column), whose partial dK and dV a merge kernel sums.
 struct BwdHostPlan {
     int32_t n_kb = 0, n_qt = 0;
-    std::vector<int32_t> kb_order;  // key blocks, most work first
-    std::vector<int32_t> kb_ptr;    // n_kb + 1
-    std::vector<int32_t> kb_runs;   // pairs: qt_begin, qt_end | (needs_mask << 31)
+    int32_t n_items = 0, n_parts = 0;
+    std::vector<int32_t> kb_order;   // work items, most work first
+    std::vector<int32_t> kb_ptr;     // n_items + 1
+    std::vector<int32_t> kb_runs;    // pairs: qt_begin, qt_end | (needs_mask << 31)
+    std::vector<int32_t> item_kb;    // key block of each item
+    std::vector<int32_t> item_part;  // -1 or the item's partial slot
+    std::vector<int32_t> split_kb;   // split key blocks and their slots
+    std::vector<int32_t> split_ptr;  // [split_ptr[s], split_ptr[s+1])
     int64_t tiles = 0, masked_tiles = 0;
 };
 
-// Key blocks of bkb keys (kBKB, or 64 with the forward's 64-row plans).
-BwdHostPlan build_bwd_plan(const MaskRule& rule, int32_t bkb);
+// Key blocks of bkb keys (kBKB, or 64 with the forward's 64-row plans);
+// split_cap as build_plan's.
+BwdHostPlan build_bwd_plan(const MaskRule& rule, int32_t bkb, int64_t split_cap = 0);
 
 // Backward arguments: the forward's (rule, plan, Q, K, V, O) plus gradients,
 // the saved log-sum-exp and the transposed plan.
@@ -216,6 +226,21 @@ struct BwdArgs {
     const int32_t* kb_ptr;
     const int32_t* kb_runs;
     int32_t n_kb;
+    // Split work items (bf16 d = 64 / 128 kernels only).  dQ: f.item_qb,
+    // f.item_part and f.n_parts of the forward plan; partials [BH][n_parts]
+    // [bq][d] fp32 in dq_part.  dK/dV: kv_item_kb, kv_item_part; partials
+    // [BH][kv_n_parts][bkb][d] fp32 for dK, then the same for dV, in kv_part.
+    int32_t n_q_items, n_kv_items;
+    float* dq_part;
+    const int32_t* dq_split_qb;
+    const int32_t* dq_split_ptr;
+    int32_t dq_n_split;
+    const int32_t* kv_item_kb;    // null: item = key block
+    const int32_t* kv_item_part;  // null: no partial slots
+    float* kv_part;
+    const int32_t* kv_split_kb;
+    const int32_t* kv_split_ptr;
+    int32_t kv_n_split, kv_n_parts;
 };
 
 int launch_bwd(int dtype, int d, const BwdArgs& args, void* stream);

@@ -305,16 +305,17 @@ HostPlan build_plan(const MaskRule& rule, int32_t bq, int32_t bk, int64_t split_
     return p;
 }
 
-BwdHostPlan build_bwd_plan(const MaskRule& rule, int32_t bkb) {
+BwdHostPlan build_bwd_plan(const MaskRule& rule, int32_t bkb, int64_t split_cap) {
     BwdHostPlan p;
     const int64_t T = rule.T();
     p.n_kb = static_cast<int32_t>((T + bkb - 1) / bkb);
     p.n_qt = static_cast<int32_t>((T + kBQB - 1) / kBQB);
     const bool any_global_row = rule.rows_global_in(0, T) > 0;
     const int64_t back = rule.band_back(), fwd = rule.band_fwd();
+    std::vector<std::vector<int32_t>> block_runs(p.n_kb);
     std::vector<int64_t> work(p.n_kb, 0);
-    p.kb_ptr.push_back(0);
     for (int32_t kb = 0; kb < p.n_kb; ++kb) {
+        std::vector<int32_t>& runs = block_runs[kb];
         const int64_t k0 = int64_t(kb) * bkb, k1 = std::min<int64_t>(T, k0 + bkb);
         // Query tiles that can hold allowed pairs: every tile when some row is
         // global, the block has column keys or in block mode; else the rows
@@ -336,25 +337,60 @@ BwdHostPlan build_bwd_plan(const MaskRule& rule, int32_t bkb) {
             }
             const bool need_mask = !(cls == SA_TILE_FULL && q0 + kBQB <= T && k0 + bkb <= T);
             const int32_t flag = need_mask ? int32_t(0x80000000u) : 0;
-            if (open && (p.kb_runs.back() & int32_t(0x80000000u)) == flag &&
-                (p.kb_runs.back() & 0x7fffffff) == qt) {
-                p.kb_runs.back() = int32_t(qt + 1) | flag;
+            if (open && (runs.back() & int32_t(0x80000000u)) == flag && (runs.back() & 0x7fffffff) == qt) {
+                runs.back() = int32_t(qt + 1) | flag;
             } else {
-                p.kb_runs.push_back(static_cast<int32_t>(qt));
-                p.kb_runs.push_back(int32_t(qt + 1) | flag);
+                runs.push_back(static_cast<int32_t>(qt));
+                runs.push_back(int32_t(qt + 1) | flag);
                 open = true;
             }
             ++tiles;
             p.masked_tiles += need_mask ? 1 : 0;
         }
-        p.kb_ptr.push_back(static_cast<int32_t>(p.kb_runs.size() / 2));
         p.tiles += tiles;
         work[kb] = tiles;
     }
-    p.kb_order.resize(p.n_kb);
+    // Work items, as in build_plan: key blocks far above the mean become
+    // ceil(tiles / cap) items over consecutive ranges of their query tiles.
+    const int64_t mean = p.n_kb ? (p.tiles + p.n_kb - 1) / p.n_kb : 0;
+    const int64_t cap = split_cap == kSplitAuto ? std::max<int64_t>(kSplitMinTiles, 2 * mean)
+                        : split_cap > 0         ? split_cap
+                                                : INT64_MAX;
+    std::vector<int64_t> item_work;
+    p.kb_ptr.push_back(0);
+    p.split_ptr.push_back(0);
+    for (int32_t kb = 0; kb < p.n_kb; ++kb) {
+        const std::vector<int32_t>& runs = block_runs[kb];
+        const int64_t w = work[kb];
+        const int64_t parts = w > cap ? (w + cap - 1) / cap : 1;
+        for (int64_t x = 0; x < parts; ++x) {
+            const int64_t t0 = w * x / parts, t1 = w * (x + 1) / parts;
+            int64_t t = 0;
+            for (size_t r = 0; r < runs.size(); r += 2) {
+                const int32_t q0 = runs[r], end = runs[r + 1];
+                const int32_t q1 = end & 0x7fffffff, flag = end & int32_t(0x80000000u);
+                const int64_t lo = std::max(t0, t), hi = std::min(t1, t + (q1 - q0));
+                if (lo < hi) {
+                    p.kb_runs.push_back(static_cast<int32_t>(q0 + (lo - t)));
+                    p.kb_runs.push_back(static_cast<int32_t>(q0 + (hi - t)) | flag);
+                }
+                t += q1 - q0;
+            }
+            p.kb_ptr.push_back(static_cast<int32_t>(p.kb_runs.size() / 2));
+            p.item_kb.push_back(kb);
+            p.item_part.push_back(parts > 1 ? p.n_parts++ : -1);
+            item_work.push_back(t1 - t0);
+        }
+        if (parts > 1) {
+            p.split_kb.push_back(kb);
+            p.split_ptr.push_back(p.n_parts);
+        }
+    }
+    p.n_items = static_cast<int32_t>(p.item_kb.size());
+    p.kb_order.resize(p.n_items);
     std::iota(p.kb_order.begin(), p.kb_order.end(), 0);
     std::stable_sort(p.kb_order.begin(), p.kb_order.end(),
-                     [&](int32_t x, int32_t y) { return work[x] > work[y]; });
+                     [&](int32_t x, int32_t y) { return item_work[x] > item_work[y]; });
     return p;
 }
 

@@ -66,13 +66,14 @@
  * frees or keeps them.  The library owns a per-device cache of execution
  * plans (tile lists for one spec and T), built on first use and freed by
  * sparse_attn_release_cache(), and an fp32 workspace per (device, stream),
- * grown on demand: the bf16 forward's partial results when a plan splits
- * a heavy query block (at most 1 GiB; past that the unsplit plan runs), the
- * backward's row dots and decode's key-split partials.  Calls are
+ * grown on demand: partial results when a plan splits a heavy block (bf16
+ * forward and backward; at most 1 GiB, past that the unsplit plan runs),
+ * the backward's row dots and decode's key-split partials.  Calls are
  * thread-safe; calls that share a stream use its workspace in stream order.
  *
  * Tuning.  SA_FWD_SPLIT_TILES=n (n > 0) in the environment makes the bf16
- * forward split every query block above n key tiles into work items (the
+ * d = 64 / 128 forward and backward split every query block (and, in the
+ * backward's dK/dV pass, every key block) above n tiles into work items (the
  * default splits blocks above max(16, twice the mean)); the result is the
  * same up to rounding order.
  *

@@ -5,7 +5,8 @@
 // order, hold exactly the block's in-place tiles (with their mask flags) and
 // its gathered key list, that gathered cuts fall on whole tiles, that the
 // partial slots and the merge lists agree, and that the item order is a
-// permutation, heaviest first.  Prints "ok <cases>" and exits 0, or prints
+// permutation, heaviest first; the backward plan's key-block items the same
+// way.  Prints "ok <cases>" and exits 0, or prints
 // the first mismatch and exits 1.
 #include <algorithm>
 #include <cstdint>
@@ -141,6 +142,65 @@ int check(const std::string& spec, int T, int bq, int64_t cap) {
     return 0;
 }
 
+// The backward plan: the items of each key block, in order, hold exactly
+// the block's query-tile runs (with their mask flags).
+int check_bwd(const std::string& spec, int T, int bkb, int64_t cap) {
+    sa_mask m;
+    if (sa::parse_mask_spec(spec.c_str(), &m) != SA_OK) return fail("spec does not parse", spec, T, bkb, cap);
+    const sa::MaskRule rule(m, T);
+    const sa::BwdHostPlan one = sa::build_bwd_plan(rule, bkb, 0);
+    const sa::BwdHostPlan sp = sa::build_bwd_plan(rule, bkb, cap);
+    if (one.n_items != one.n_kb || one.n_parts != 0) return fail("bwd: unsplit plan has split items", spec, T, bkb, cap);
+    if (sp.tiles != one.tiles || sp.masked_tiles != one.masked_tiles) return fail("bwd: totals differ", spec, T, bkb, cap);
+    auto tiles_of = [](const sa::BwdHostPlan& p, int it) {
+        std::vector<int32_t> out;
+        for (int r = p.kb_ptr[it]; r < p.kb_ptr[it + 1]; ++r) {
+            const int32_t q0 = p.kb_runs[2 * r], end = p.kb_runs[2 * r + 1];
+            for (int32_t q = q0; q < (end & 0x7fffffff); ++q) out.push_back(q | (end & int32_t(0x80000000u)));
+        }
+        return out;
+    };
+    const int64_t mean = one.n_kb ? (one.tiles + one.n_kb - 1) / one.n_kb : 0;
+    const int64_t eff = cap == sa::kSplitAuto ? std::max<int64_t>(sa::kSplitMinTiles, 2 * mean) : cap;
+    int it = 0, parts = 0;
+    std::vector<int64_t> work(sp.n_items, 0);
+    for (int kb = 0; kb < one.n_kb; ++kb) {
+        const std::vector<int32_t> want = tiles_of(one, kb);
+        std::vector<int32_t> got;
+        const int first = it;
+        while (it < sp.n_items && sp.item_kb[it] == kb) {
+            const std::vector<int32_t> t = tiles_of(sp, it);
+            work[it] = int64_t(t.size());
+            if (t.empty() && !want.empty()) return fail("bwd: empty item", spec, T, bkb, cap);
+            got.insert(got.end(), t.begin(), t.end());
+            ++it;
+        }
+        const int n = it - first;
+        if (n == 0) return fail("bwd: block without items", spec, T, bkb, cap);
+        if (got != want) return fail("bwd: query tiles differ", spec, T, bkb, cap);
+        const int64_t w = int64_t(want.size());
+        if (n != (w > eff ? (w + eff - 1) / eff : 1)) return fail("bwd: item count", spec, T, bkb, cap);
+        for (int x = first; x < it; ++x)
+            if (sp.item_part[x] != (n > 1 ? parts + (x - first) : -1)) return fail("bwd: partial slot", spec, T, bkb, cap);
+        if (n > 1) {
+            size_t s = 0;
+            while (s < sp.split_kb.size() && sp.split_kb[s] != kb) ++s;
+            if (s == sp.split_kb.size() || sp.split_ptr[s] != parts || sp.split_ptr[s + 1] != parts + n)
+                return fail("bwd: merge list", spec, T, bkb, cap);
+            parts += n;
+        }
+    }
+    if (it != sp.n_items || parts != sp.n_parts) return fail("bwd: item or part count", spec, T, bkb, cap);
+    std::vector<char> seen(sp.n_items, 0);
+    for (int x = 0; x < sp.n_items; ++x) {
+        const int32_t o = sp.kb_order[x];
+        if (o < 0 || o >= sp.n_items || seen[o]) return fail("bwd: order is not a permutation", spec, T, bkb, cap);
+        seen[o] = 1;
+        if (x > 0 && work[sp.kb_order[x - 1]] < work[o]) return fail("bwd: order not heaviest first", spec, T, bkb, cap);
+    }
+    return 0;
+}
+
 }  // namespace
 
 int main() {
@@ -156,7 +216,8 @@ int main() {
     for (const auto& f : fixed)
         for (int64_t cap : {int64_t(sa::kSplitAuto), int64_t(1), int64_t(7), int64_t(60)}) {
             if (check(f.spec, f.T, f.bq, cap)) return 1;
-            ++cases;
+            if (check_bwd(f.spec, f.T, f.bq == 64 ? 64 : 128, cap)) return 1;
+            cases += 2;
         }
     for (int n = 0; n < 400; ++n) {
         const int T = 1 + r.below(n < 200 ? 700 : 3000);
@@ -165,7 +226,8 @@ int main() {
         const int64_t caps[] = {sa::kSplitAuto, 1, 2, 3, 5, 16};
         const int64_t cap = caps[r.below(6)];
         if (check(spec, T, bq, cap)) return 1;
-        ++cases;
+        if (check_bwd(spec, T, bq == 64 ? 64 : 128, cap)) return 1;
+        cases += 2;
     }
     std::printf("ok %d\n", cases);
     return 0;

@@ -126,6 +126,27 @@ def test_backward_block_mode_64_row_tiles(gpu, T):
         assert gpu.sparse_attn_plan_info(spec, T, 64)["bq"] == 64
         full_check(gpu, spec, 2, 2, T, 64, "bf16", seed=T)
 
+@pytest.mark.parametrize("cap", [1, 2, 3])
+@pytest.mark.parametrize("spec,T,d", [
+    ("bidir;radius=64;stride=16;phase=0;global=0:128", 700, 64),
+    ("causal;window=64;stride=8;phase=3;global=5:9", 500, 128),
+    ("causal;window=100;global=300:340", 650, 128),
+    ("blocks;block=64;radius=1;random=3;seed=0;global=0:128", 900, 64),
+])
+def test_backward_split_forced(gpu, monkeypatch, spec, T, d, cap):
+    """Every query block (dQ pass) and key block (dK/dV pass) above `cap`
+    tiles split into items whose partials the merge kernels sum."""
+    monkeypatch.setenv("SA_FWD_SPLIT_TILES", str(cap))
+    full_check(gpu, spec, 2, 2, T, d, "bf16", seed=cap)
+
+
+def test_backward_global_rows_automatic(gpu):
+    """Global rows 0..127 of a 2K bidirectional layer: their query block and
+    the key blocks of the global columns read every tile, so both passes
+    split them by themselves."""
+    full_check(gpu, "bidir;radius=64;stride=16;phase=0;global=0:128", 1, 3, 2048, 128, "bf16", seed=7)
+
+
 @pytest.mark.parametrize("case", range(80))
 def test_backward_random_specs(gpu, case):
     """Seeded random specs (all modes and fields, ragged lengths up to 600):
