@@ -49,6 +49,8 @@ WORKLOADS = {
                                  specs=["blocks;block=64;radius=1;random=3;seed=0;global=0:128"]),
     "mistral32k_window4096_bwd": dict(kind="backward", B=1, H=32, T=32768, d=128, dtype="bf16",
                                       specs=["causal;window=4096"]),
+    "longformer16k_r256_s16_g128_bwd": dict(kind="backward", B=1, H=16, T=16384, d=64, dtype="bf16",
+                                            specs=["bidir;radius=256;stride=16;phase=0;global=0:128"]),
     "bigbird4k_b8_h12_d64_bwd": dict(kind="backward", B=8, H=12, T=4096, d=64, dtype="bf16",
                                      specs=["blocks;block=64;radius=1;random=3;seed=0;global=0:128"]),
     "mistral_decode_b64_w4096": dict(kind="decode", B=64, H=32, Hkv=8, d=128, dtype="bf16",

@@ -125,24 +125,26 @@ class PlanCache {
     }
 
     // The backward plan (key blocks -> query tiles) for (spec, T).
-    int get_bwd(const sa_mask& m, int T, int bkb, int64_t split_cap, sa::BwdDevicePlan* out) {
+    int get_bwd(const sa_mask& m, int T, int bkb, int64_t split_cap, bool gather, sa::BwdDevicePlan* out) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return SA_ERR_HIP;
         std::string key = sa::canonical_spec(m) + "|T=" + std::to_string(T) + "|bwd|bkb=" +
                           std::to_string(bkb) + "|split=" + std::to_string(split_cap) +
-                          "|dev=" + std::to_string(dev);
+                          (gather ? "|gather" : "") + "|dev=" + std::to_string(dev);
         std::lock_guard<std::mutex> lock(mu_);
         auto it = bwd_.find(key);
         if (it != bwd_.end()) {
             *out = it->second.plan;
             return SA_OK;
         }
-        sa::BwdHostPlan hp = sa::build_bwd_plan(MaskRule(m, T), bkb, split_cap);
+        sa::BwdHostPlan hp = sa::build_bwd_plan(MaskRule(m, T), bkb, split_cap, gather);
         sa::BwdDevicePlan dp;
         dp.n_kb = hp.n_kb;
         dp.n_items = hp.n_items;
         dp.n_parts = hp.n_parts;
         dp.n_split = static_cast<int32_t>(hp.split_kb.size());
+        dp.n_gkb = hp.n_gkb;
+        dp.n_col = hp.n_col;
         size_t off = 0;
         auto section = [&](size_t bytes, size_t* where) {
             off = align_up(off, 16);
@@ -407,7 +409,7 @@ int backward(int dtype, const void* Q, const void* K, const void* V, const void*
     rc = cache().get(m, T, bq, cap, &dp);
     if (rc != SA_OK) return rc;
     sa::BwdDevicePlan bp;
-    rc = cache().get_bwd(m, T, bkb, cap, &bp);
+    rc = cache().get_bwd(m, T, bkb, cap, dma, &bp);
     if (rc != SA_OK) return rc;
     // Workspace: row dots D_i, then dQ partials, then dK and dV partials
     // (each section 256-byte aligned).  Past kMaxSplitWorkspace of partials
@@ -424,7 +426,7 @@ int backward(int dtype, const void* Q, const void* K, const void* V, const void*
     size_t wbytes = sized(dp, bp, &q_off, &kv_off);
     if (wbytes - align_up(lbytes, 256) > kMaxSplitWorkspace) {
         rc = cache().get(m, T, bq, 0, &dp);
-        if (rc == SA_OK) rc = cache().get_bwd(m, T, bkb, 0, &bp);
+        if (rc == SA_OK) rc = cache().get_bwd(m, T, bkb, 0, dma, &bp);
         if (rc != SA_OK) return rc;
         wbytes = sized(dp, bp, &q_off, &kv_off);
     }
@@ -491,6 +493,8 @@ int backward(int dtype, const void* Q, const void* K, const void* V, const void*
     b.kv_split_ptr = reinterpret_cast<const int32_t*>(bb + bp.off_split_ptr);
     b.kv_n_split = bp.n_split;
     b.kv_n_parts = bp.n_parts;
+    b.kv_n_gkb = bp.n_gkb;
+    b.kv_n_col = bp.n_col;
     if (BH * int64_t(std::max(dp.n_items, bp.n_items)) > INT32_MAX) return SA_ERR_SHAPE;
     return sa::launch_bwd(dtype, d, b, stream);
 }

@@ -667,6 +667,9 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kerne
     const int bh = work / n_items;
     const int it = ldc(b.kb_order, work % n_items);  // a key block or one query range of it
     const int kb = ldc(b.kv_item_kb, it);
+    // Gathered block kb - n_kb: keys f.colkeys[slot]; a band block skips its
+    // column keys when they are gathered.
+    const bool gath = kb >= b.n_kb;
     const int T = a.T;
     const size_t base = size_t(bh) * size_t(T) * D;
     const E* Qp = static_cast<const E*>(a.Q) + base;
@@ -675,12 +678,16 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kerne
     const E* Gp = static_cast<const E*>(b.dO) + base;
     const float* Lp = b.lse + size_t(bh) * size_t(T);
     const float* Dp = b.Dw + size_t(bh) * size_t(T);
-    const int kj = kb * (NW * 32) + wave * 32 + n;
+    const int gslot = (kb - b.n_kb) * (NW * 32) + wave * 32 + n;
+    const int kj = gath ? a.colkeys[min(gslot, b.kv_n_col - 1)] : kb * (NW * 32) + wave * 32 + n;
 
     F kf[S::NKS], vf[S::NKS];
     load_frags<E, D>(kf, Kp, kj, T, h);
     load_frags<E, D>(vf, Vp, kj, T, h);
     const bool colj = kj < T && ((a.colbits[kj >> 6] >> (kj & 63)) & 1);
+    // This lane's key takes part: gathered keys inside the list; band keys
+    // below T, column keys only when they are not gathered.
+    const bool mine = gath ? gslot < b.kv_n_col : (kj < T && !(colj && b.kv_n_gkb > 0));
 
     f32x16 dk[S::NDB], dv[S::NDB];
 #pragma unroll
@@ -715,7 +722,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kerne
             const int w0 = q0 >> 5, nw = (T + 31) >> 5;
             if (w0 < nw) roww = ldc(a.rowbits, w0);
             if (w0 + 1 < nw) roww |= uint64_t(ldc(a.rowbits, w0 + 1)) << 32;
-            aw = kj < T ? allowed_word_T(a, kj, q0, colj, roww) : 0ull;
+            aw = mine ? allowed_word_T(a, kj, q0, colj, roww) : 0ull;
         }
         // S and dP for both 32-query halves, then per half P and dS,
         // dV^T += dO^T P and dK^T += Q^T dS.
@@ -822,9 +829,10 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kerne
     if (part >= 0) {  // one query range of a split key block: unscaled partials
         const size_t slot = (size_t(bh) * b.kv_n_parts + part) * (NW * 32) * D;
         const size_t half = size_t(a.BH) * b.kv_n_parts * (NW * 32) * D;
-        store_rows_f32<D>(b.kv_part + slot, dk, kj - kb * (NW * 32), h);
-        store_rows_f32<D>(b.kv_part + half + slot, dv, kj - kb * (NW * 32), h);
-    } else if (kj < T) {
+        // row of this lane's key in the block (band or gathered)
+        store_rows_f32<D>(b.kv_part + slot, dk, wave * 32 + n, h);
+        store_rows_f32<D>(b.kv_part + half + slot, dv, wave * 32 + n, h);
+    } else if (mine) {
         store_rows<E, D>(static_cast<E*>(b.dK) + base, dk, kj, h, b.scale);
         store_rows<E, D>(static_cast<E*>(b.dV) + base, dv, kj, h, 1.f);
     }
@@ -832,19 +840,33 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kerne
 
 // Sum the partials of the split blocks into the bf16 output: rows of block
 // split_blk[s] get mul * the sum over slots [split_ptr[s], split_ptr[s+1])
-// of part[bh][slot][row][:].  One thread per (row, 4 columns).
+// of part[bh][slot][row][:].  Row r of block blk is output row blk * rows
+// + r (skipped if colbits marks it a column key), or, for a gathered block
+// blk >= n_band, output row colkeys[(blk - n_band) * rows + r] while that
+// is below n_col.  One thread per (row, 4 columns).
 template <int D>
 __global__ __launch_bounds__(256) void sa_bwd_sum_parts_kernel(const float* part, int n_parts, int rows,
                                                                 const int32_t* split_blk,
                                                                 const int32_t* split_ptr, int n_split,
-                                                                __bf16* dst, int T, float mul) {
+                                                                __bf16* dst, int T, float mul,
+                                                                const uint64_t* colbits,
+                                                                const int32_t* colkeys, int n_col,
+                                                                int n_band) {
     constexpr int C = D / 4, RPW = 256 / C;
     const int per_blk = rows / RPW;
     const int x = blockIdx.x % per_blk, y = blockIdx.x / per_blk;
     const int bh = y / n_split, sidx = y % n_split;
     const int r = x * RPW + threadIdx.x / C, c = threadIdx.x % C;
-    const int row = split_blk[sidx] * rows + r;
-    if (row >= T) return;
+    const int blk = split_blk[sidx];
+    int row;
+    if (blk >= n_band) {
+        const int slot = (blk - n_band) * rows + r;
+        if (slot >= n_col) return;
+        row = colkeys[slot];
+    } else {
+        row = blk * rows + r;
+        if (row >= T || (colbits && ((colbits[row >> 6] >> (row & 63)) & 1))) return;
+    }
     float4 sum = {0.f, 0.f, 0.f, 0.f};
     for (int p = split_ptr[sidx]; p < split_ptr[sidx + 1]; ++p) {
         const float4 v =
@@ -881,18 +903,22 @@ int launch_b_dma(const BwdArgs& b, void* stream) {
     constexpr int ROWS = NW * 32;  // query rows of a dQ block, keys of a dK/dV block
     const auto st = static_cast<hipStream_t>(stream);
     auto sum_parts = [&](const float* part, int n_parts, const int32_t* blk, const int32_t* ptr, int n_split,
-                         void* dst, float mul) {
+                         void* dst, float mul, bool kv) {
         const int64_t g = int64_t(b.f.BH) * n_split * (ROWS / (256 / (D / 4)));
         if (g > INT32_MAX) return SA_ERR_SHAPE;
+        const bool gathered = kv && b.kv_n_gkb > 0;
         hipLaunchKernelGGL((sa_bwd_sum_parts_kernel<D>), dim3(static_cast<unsigned>(g)), dim3(256), 0, st, part,
-                           n_parts, ROWS, blk, ptr, n_split, static_cast<__bf16*>(dst), b.f.T, mul);
+                           n_parts, ROWS, blk, ptr, n_split, static_cast<__bf16*>(dst), b.f.T, mul,
+                           gathered ? b.f.colbits : nullptr, b.f.colkeys, b.kv_n_col,
+                           gathered ? b.n_kb : INT32_MAX);
         return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
     };
     const unsigned g1 = static_cast<unsigned>(int64_t(b.f.BH) * b.n_q_items);
     hipLaunchKernelGGL((sa_bwd_dq_dma_kernel<D, NW>), dim3(g1), dim3(NW * 64), 0, st, b);
     if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
     if (b.f.n_parts > 0) {
-        const int rc = sum_parts(b.dq_part, b.f.n_parts, b.dq_split_qb, b.dq_split_ptr, b.dq_n_split, b.dQ, b.scale);
+        const int rc =
+            sum_parts(b.dq_part, b.f.n_parts, b.dq_split_qb, b.dq_split_ptr, b.dq_n_split, b.dQ, b.scale, false);
         if (rc != SA_OK) return rc;
     }
     const unsigned g2 = static_cast<unsigned>(int64_t(b.f.BH) * b.n_kv_items);
@@ -900,9 +926,11 @@ int launch_b_dma(const BwdArgs& b, void* stream) {
     if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
     if (b.kv_n_parts > 0) {
         const size_t half = size_t(b.f.BH) * b.kv_n_parts * ROWS * D;
-        int rc = sum_parts(b.kv_part, b.kv_n_parts, b.kv_split_kb, b.kv_split_ptr, b.kv_n_split, b.dK, b.scale);
+        int rc = sum_parts(b.kv_part, b.kv_n_parts, b.kv_split_kb, b.kv_split_ptr, b.kv_n_split, b.dK, b.scale,
+                           true);
         if (rc == SA_OK)
-            rc = sum_parts(b.kv_part + half, b.kv_n_parts, b.kv_split_kb, b.kv_split_ptr, b.kv_n_split, b.dV, 1.f);
+            rc = sum_parts(b.kv_part + half, b.kv_n_parts, b.kv_split_kb, b.kv_split_ptr, b.kv_n_split, b.dV, 1.f,
+                           true);
         if (rc != SA_OK) return rc;
     }
     return SA_OK;

@@ -4,6 +4,8 @@
 
 #include <stdint.h>
 
+#include <algorithm>
+
 #include <string>
 #include <vector>
 
@@ -68,6 +70,11 @@ class MaskRule {
     int64_t key_limit(int64_t i) const { return causal() ? i : T_ - 1; }
     // Allowed keys of row i within [a, b).
     int64_t allowed_in(int64_t i, int64_t a, int64_t b) const;
+    // Of those, the ones that are not column (strided or global) keys.
+    int64_t allowed_noncol_in(int64_t i, int64_t a, int64_t b) const {
+        const int64_t lo = std::max<int64_t>(a, 0), hi = std::min<int64_t>(b, key_limit(i) + 1);
+        return lo >= hi ? 0 : allowed_in(i, a, b) - col_keys_in(lo, hi);
+    }
     // SA_TILE_* for rows [q0, q1) x keys [k0, k1), judged on in-range cells.
     int classify(int64_t q0, int64_t q1, int64_t k0, int64_t k1) const;
     // Distance bounds of the band: key j is in row i's band iff
@@ -137,7 +144,7 @@ struct DevicePlan {
 struct BwdDevicePlan {
     void* base = nullptr;
     size_t bytes = 0;
-    int32_t n_kb = 0, n_items = 0, n_parts = 0, n_split = 0;
+    int32_t n_kb = 0, n_items = 0, n_parts = 0, n_split = 0, n_gkb = 0, n_col = 0;
     size_t off_order = 0, off_ptr = 0, off_runs = 0, off_item_kb = 0, off_item_part = 0,
            off_split_kb = 0, off_split_ptr = 0;
 };
@@ -196,6 +203,10 @@ constexpr int kBQB = 64;   // queries per tile it visits
 // column), whose partial dK and dV a merge kernel sums.
 struct BwdHostPlan {
     int32_t n_kb = 0, n_qt = 0;
+    // With gathered column keys: key blocks n_kb .. n_kb + n_gkb - 1 are
+    // blocks of the sorted column-key list (n_col keys), and the band blocks
+    // leave their column keys to them.
+    int32_t n_gkb = 0, n_col = 0;
     int32_t n_items = 0, n_parts = 0;
     std::vector<int32_t> kb_order;   // work items, most work first
     std::vector<int32_t> kb_ptr;     // n_items + 1
@@ -208,8 +219,10 @@ struct BwdHostPlan {
 };
 
 // Key blocks of bkb keys (kBKB, or 64 with the forward's 64-row plans);
-// split_cap as build_plan's.
-BwdHostPlan build_bwd_plan(const MaskRule& rule, int32_t bkb, int64_t split_cap = 0);
+// split_cap as build_plan's; gather_cols: run the column keys as gathered
+// key blocks (bf16 d = 64 / 128 kernels).
+BwdHostPlan build_bwd_plan(const MaskRule& rule, int32_t bkb, int64_t split_cap = 0,
+                           bool gather_cols = false);
 
 // Backward arguments: the forward's (rule, plan, Q, K, V, O) plus gradients,
 // the saved log-sum-exp and the transposed plan.
@@ -241,6 +254,10 @@ struct BwdArgs {
     const int32_t* kv_split_kb;
     const int32_t* kv_split_ptr;
     int32_t kv_n_split, kv_n_parts;
+    // Gathered column keys (kv_n_gkb > 0): items with key block kb >= n_kb
+    // run keys f.colkeys[(kb - n_kb) * bkb ...] (kv_n_col keys in all), and
+    // band blocks skip their column keys.
+    int32_t kv_n_gkb, kv_n_col;
 };
 
 int launch_bwd(int dtype, int d, const BwdArgs& args, void* stream);

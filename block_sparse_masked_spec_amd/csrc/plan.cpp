@@ -305,23 +305,34 @@ HostPlan build_plan(const MaskRule& rule, int32_t bq, int32_t bk, int64_t split_
     return p;
 }
 
-BwdHostPlan build_bwd_plan(const MaskRule& rule, int32_t bkb, int64_t split_cap) {
+BwdHostPlan build_bwd_plan(const MaskRule& rule, int32_t bkb, int64_t split_cap, bool gather_cols) {
     BwdHostPlan p;
     const int64_t T = rule.T();
     p.n_kb = static_cast<int32_t>((T + bkb - 1) / bkb);
     p.n_qt = static_cast<int32_t>((T + kBQB - 1) / kBQB);
     const bool any_global_row = rule.rows_global_in(0, T) > 0;
     const int64_t back = rule.band_back(), fwd = rule.band_fwd();
-    std::vector<std::vector<int32_t>> block_runs(p.n_kb);
-    std::vector<int64_t> work(p.n_kb, 0);
+    // A column key is allowed for every row its causal limit lets read it,
+    // so in the band blocks it would make every query tile live.  With
+    // gather_cols the column keys run as dense blocks of their own (every
+    // query tile from the first that may read them), and the band blocks
+    // count and execute only their other keys.
+    std::vector<int32_t> colkeys;
+    if (gather_cols)
+        for (int64_t j = 0; j < T; ++j)
+            if (rule.col_key(j)) colkeys.push_back(static_cast<int32_t>(j));
+    p.n_col = static_cast<int32_t>(colkeys.size());
+    p.n_gkb = static_cast<int32_t>((colkeys.size() + bkb - 1) / bkb);
+    std::vector<std::vector<int32_t>> block_runs(p.n_kb + p.n_gkb);
+    std::vector<int64_t> work(p.n_kb + p.n_gkb, 0);
     for (int32_t kb = 0; kb < p.n_kb; ++kb) {
         std::vector<int32_t>& runs = block_runs[kb];
         const int64_t k0 = int64_t(kb) * bkb, k1 = std::min<int64_t>(T, k0 + bkb);
         // Query tiles that can hold allowed pairs: every tile when some row is
-        // global, the block has column keys or in block mode; else the rows
-        // whose band meets the block.
+        // global, the block has column keys (not gathered) or in block mode;
+        // else the rows whose band meets the block.
         int64_t qlo = 0, qhi = T - 1;
-        if (!any_global_row && rule.col_keys_in(k0, k1) == 0 && rule.block() == 0) {
+        if (!any_global_row && (gather_cols || rule.col_keys_in(k0, k1) == 0) && rule.block() == 0) {
             qlo = fwd >= T ? 0 : std::max<int64_t>(0, k0 - fwd);
             qhi = back >= T ? T - 1 : std::min<int64_t>(T - 1, k1 - 1 + back);
             if (rule.causal()) qlo = std::max(qlo, k0);
@@ -330,7 +341,14 @@ BwdHostPlan build_bwd_plan(const MaskRule& rule, int32_t bkb, int64_t split_cap)
         int64_t tiles = 0;
         for (int64_t qt = qlo / kBQB; qt <= qhi / kBQB && qt < p.n_qt; ++qt) {
             const int64_t q0 = qt * kBQB, q1 = std::min<int64_t>(T, q0 + kBQB);
-            const int cls = rule.classify(q0, q1, k0, k1);
+            int cls;
+            if (gather_cols) {
+                int64_t n = 0;
+                for (int64_t i = q0; i < q1; ++i) n += rule.allowed_noncol_in(i, k0, k1);
+                cls = n == 0 ? SA_TILE_EMPTY : (n == (q1 - q0) * (k1 - k0) ? SA_TILE_FULL : SA_TILE_PARTIAL);
+            } else {
+                cls = rule.classify(q0, q1, k0, k1);
+            }
             if (cls == SA_TILE_EMPTY) {
                 open = false;
                 continue;
@@ -350,16 +368,28 @@ BwdHostPlan build_bwd_plan(const MaskRule& rule, int32_t bkb, int64_t split_cap)
         p.tiles += tiles;
         work[kb] = tiles;
     }
+    // Gathered blocks: every query tile from the first row that may read the
+    // block's first key, each evaluating the rule (causal limit, ragged ends).
+    for (int32_t c = 0; c < p.n_gkb; ++c) {
+        const int64_t first = rule.causal() ? colkeys[size_t(c) * bkb] / kBQB : 0;
+        if (first < p.n_qt) {
+            block_runs[p.n_kb + c] = {static_cast<int32_t>(first), p.n_qt | int32_t(0x80000000u)};
+            work[p.n_kb + c] = p.n_qt - first;
+            p.tiles += p.n_qt - first;
+            p.masked_tiles += p.n_qt - first;
+        }
+    }
     // Work items, as in build_plan: key blocks far above the mean become
     // ceil(tiles / cap) items over consecutive ranges of their query tiles.
-    const int64_t mean = p.n_kb ? (p.tiles + p.n_kb - 1) / p.n_kb : 0;
+    const int32_t n_blocks = p.n_kb + p.n_gkb;
+    const int64_t mean = n_blocks ? (p.tiles + n_blocks - 1) / n_blocks : 0;
     const int64_t cap = split_cap == kSplitAuto ? std::max<int64_t>(kSplitMinTiles, 2 * mean)
                         : split_cap > 0         ? split_cap
                                                 : INT64_MAX;
     std::vector<int64_t> item_work;
     p.kb_ptr.push_back(0);
     p.split_ptr.push_back(0);
-    for (int32_t kb = 0; kb < p.n_kb; ++kb) {
+    for (int32_t kb = 0; kb < n_blocks; ++kb) {
         const std::vector<int32_t>& runs = block_runs[kb];
         const int64_t w = work[kb];
         const int64_t parts = w > cap ? (w + cap - 1) / cap : 1;

@@ -144,13 +144,32 @@ int check(const std::string& spec, int T, int bq, int64_t cap) {
 
 // The backward plan: the items of each key block, in order, hold exactly
 // the block's query-tile runs (with their mask flags).
-int check_bwd(const std::string& spec, int T, int bkb, int64_t cap) {
+int check_bwd(const std::string& spec, int T, int bkb, int64_t cap, bool gather) {
     sa_mask m;
     if (sa::parse_mask_spec(spec.c_str(), &m) != SA_OK) return fail("spec does not parse", spec, T, bkb, cap);
     const sa::MaskRule rule(m, T);
-    const sa::BwdHostPlan one = sa::build_bwd_plan(rule, bkb, 0);
-    const sa::BwdHostPlan sp = sa::build_bwd_plan(rule, bkb, cap);
-    if (one.n_items != one.n_kb || one.n_parts != 0) return fail("bwd: unsplit plan has split items", spec, T, bkb, cap);
+    const sa::BwdHostPlan one = sa::build_bwd_plan(rule, bkb, 0, gather);
+    const sa::BwdHostPlan sp = sa::build_bwd_plan(rule, bkb, cap, gather);
+    if (one.n_items != one.n_kb + one.n_gkb || one.n_parts != 0)
+        return fail("bwd: unsplit plan has split items", spec, T, bkb, cap);
+    // Every allowed pair (i, j) lies in a listed tile: query tile i / 64 of
+    // key block j / bkb, or, for a gathered column key, of its gathered block.
+    if (T <= 300) {
+        std::vector<std::vector<char>> live(one.n_kb + one.n_gkb, std::vector<char>(one.n_qt, 0));
+        for (int blk = 0; blk < one.n_kb + one.n_gkb; ++blk)
+            for (int r = one.kb_ptr[blk]; r < one.kb_ptr[blk + 1]; ++r)
+                for (int32_t q = one.kb_runs[2 * r]; q < (one.kb_runs[2 * r + 1] & 0x7fffffff); ++q) live[blk][q] = 1;
+        int ci = 0;
+        for (int64_t j = 0; j < T; ++j) {
+            const bool gathered = gather && rule.col_key(j);
+            const int blk = gathered ? one.n_kb + ci / bkb : int(j / bkb);
+            for (int64_t i = 0; i < T; ++i)
+                if (rule.allowed_in(i, j, j + 1) && !live[blk][i / sa::kBQB])
+                    return fail("bwd: allowed pair outside the plan", spec, T, bkb, cap);
+            ci += gathered ? 1 : 0;
+        }
+        if (ci != one.n_col) return fail("bwd: column key count", spec, T, bkb, cap);
+    }
     if (sp.tiles != one.tiles || sp.masked_tiles != one.masked_tiles) return fail("bwd: totals differ", spec, T, bkb, cap);
     auto tiles_of = [](const sa::BwdHostPlan& p, int it) {
         std::vector<int32_t> out;
@@ -160,11 +179,12 @@ int check_bwd(const std::string& spec, int T, int bkb, int64_t cap) {
         }
         return out;
     };
-    const int64_t mean = one.n_kb ? (one.tiles + one.n_kb - 1) / one.n_kb : 0;
+    const int nb = one.n_kb + one.n_gkb;
+    const int64_t mean = nb ? (one.tiles + nb - 1) / nb : 0;
     const int64_t eff = cap == sa::kSplitAuto ? std::max<int64_t>(sa::kSplitMinTiles, 2 * mean) : cap;
     int it = 0, parts = 0;
     std::vector<int64_t> work(sp.n_items, 0);
-    for (int kb = 0; kb < one.n_kb; ++kb) {
+    for (int kb = 0; kb < nb; ++kb) {
         const std::vector<int32_t> want = tiles_of(one, kb);
         std::vector<int32_t> got;
         const int first = it;
@@ -216,8 +236,9 @@ int main() {
     for (const auto& f : fixed)
         for (int64_t cap : {int64_t(sa::kSplitAuto), int64_t(1), int64_t(7), int64_t(60)}) {
             if (check(f.spec, f.T, f.bq, cap)) return 1;
-            if (check_bwd(f.spec, f.T, f.bq == 64 ? 64 : 128, cap)) return 1;
-            cases += 2;
+            if (check_bwd(f.spec, f.T, f.bq == 64 ? 64 : 128, cap, false)) return 1;
+            if (check_bwd(f.spec, f.T, f.bq == 64 ? 64 : 128, cap, true)) return 1;
+            cases += 3;
         }
     for (int n = 0; n < 400; ++n) {
         const int T = 1 + r.below(n < 200 ? 700 : 3000);
@@ -226,8 +247,9 @@ int main() {
         const int64_t caps[] = {sa::kSplitAuto, 1, 2, 3, 5, 16};
         const int64_t cap = caps[r.below(6)];
         if (check(spec, T, bq, cap)) return 1;
-        if (check_bwd(spec, T, bq == 64 ? 64 : 128, cap)) return 1;
-        cases += 2;
+        if (check_bwd(spec, T, bq == 64 ? 64 : 128, cap, false)) return 1;
+        if (check_bwd(spec, T, bq == 64 ? 64 : 128, cap, true)) return 1;
+        cases += 3;
     }
     std::printf("ok %d\n", cases);
     return 0;

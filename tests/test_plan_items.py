@@ -29,4 +29,4 @@ def test_split_items_cover_each_block_exactly(tmp_path):
     assert build.returncode == 0, build.stderr[-2000:]
     run = subprocess.run([exe], capture_output=True, text=True, timeout=300)
     assert run.returncode == 0 and run.stdout.startswith("ok"), run.stdout[-2000:] + run.stderr[-2000:]
-    assert int(run.stdout.split()[1]) >= 800
+    assert int(run.stdout.split()[1]) >= 1200
