@@ -342,7 +342,7 @@ BwdHostPlan build_bwd_plan(const MaskRule& rule, int32_t bkb, int64_t split_cap,
         for (int64_t qt = qlo / kBQB; qt <= qhi / kBQB && qt < p.n_qt; ++qt) {
             const int64_t q0 = qt * kBQB, q1 = std::min<int64_t>(T, q0 + kBQB);
             int cls;
-            if (gather_cols) {
+            if (gather_cols && rule.col_keys_in(k0, k1) > 0) {  // count the block's other keys
                 int64_t n = 0;
                 for (int64_t i = q0; i < q1; ++i) n += rule.allowed_noncol_in(i, k0, k1);
                 cls = n == 0 ? SA_TILE_EMPTY : (n == (q1 - q0) * (k1 - k0) ? SA_TILE_FULL : SA_TILE_PARTIAL);
