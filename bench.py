@@ -21,6 +21,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -397,6 +398,16 @@ def main():
     ms_per_step = gpu_ms / args.steps
     launches = args.steps * len(specs)
     ms_per_launch = gpu_ms / launches
+    # After the timed region: the same number of steps timed one by one, for
+    # the median step time (each bracketed by its own events on the stream).
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record(stream)
+        step(args.warmup + args.steps + i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms_median = float(statistics.median(e0.elapsed_time(e1) for e0, e1 in evs))
     secs = ms_per_step / 1e3
     eff_tflops = flops / secs / 1e12
     peak = BF16_PEAK_TFLOPS if dtype == "bf16" else F32_PEAK_TFLOPS
@@ -423,6 +434,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_median": ms_median,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
