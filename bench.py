@@ -102,6 +102,19 @@ def bwd_kernel_names(dtype: str, d: int) -> str:
     return "sa_bwd_dq_kernel + sa_bwd_dkv_kernel"
 
 
+def median_step_ms(step, n, stream):
+    """Median time of n steps, each timed alone with its own events on the
+    stream (run after the timed region; the contract's figure is the mean)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return float(statistics.median(e0.elapsed_time(e1) for e0, e1 in evs))
+
+
 def load_counter(workload: str, field: str = "hbm_bytes_per_launch"):
     """A figure from the committed counter summary (HBM bytes per launch, or
     the MFMA-busy fraction), or None once the kernel source has changed."""
@@ -211,6 +224,7 @@ def backward_bench(args, wl):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
+    ms_median = median_step_ms(step, args.steps, stream)
     secs = ms / 1e3
     tf = flops / secs / 1e12
     result = {
@@ -221,6 +235,7 @@ def backward_bench(args, wl):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": ms_median,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -282,6 +297,7 @@ def decode_bench(args, wl):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
+    ms_median = median_step_ms(step, args.steps, stream)
     secs = ms / 1e3
     # Algorithmic bytes: every allowed K and V row once, Q read, O written.
     kv_rows = min(C, rows) if rows else C
@@ -296,6 +312,7 @@ def decode_bench(args, wl):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": ms_median,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
