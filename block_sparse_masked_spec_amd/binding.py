@@ -97,7 +97,7 @@ def load():
     lib.sparse_attn_count.restype = i32
     lib.sparse_attn_tile_map.argtypes = [cs, i32, i32, i32, vp]
     lib.sparse_attn_tile_map.restype = i32
-    lib.sparse_attn_tile_shape.argtypes = [i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.sparse_attn_tile_shape.argtypes = [cs, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.sparse_attn_tile_shape.restype = i32
     lib.sparse_attn_plan_info.argtypes = [cs, i32, i32, i32, ctypes.POINTER(sa_plan_info)]
     lib.sparse_attn_plan_info.restype = i32
@@ -194,9 +194,11 @@ def sparse_attn_tile_map(mask_spec, T, bq, bk):
     return out[:nqb * nkb].reshape(nqb, nkb)
 
 
-def sparse_attn_tile_shape(d, dtype=SA_DTYPE_BF16):
+def sparse_attn_tile_shape(mask_spec, d, dtype=SA_DTYPE_BF16):
+    """(bq, bk) of the forward for mask_spec (None: token-level specs)."""
     bq, bk = ctypes.c_int(0), ctypes.c_int(0)
-    _check(load().sparse_attn_tile_shape(d, dtype, ctypes.byref(bq), ctypes.byref(bk)),
+    spec = None if mask_spec is None else _spec(mask_spec)
+    _check(load().sparse_attn_tile_shape(spec, d, dtype, ctypes.byref(bq), ctypes.byref(bk)),
            "sparse_attn_tile_shape")
     return bq.value, bk.value
 

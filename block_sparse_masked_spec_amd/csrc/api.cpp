@@ -7,9 +7,12 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <new>
+#include <sstream>
 #include <string>
+#include <thread>
 #include <unordered_map>
 
 #include "internal.hpp"
@@ -52,11 +55,76 @@ int64_t split_cap() {
     return n > 0 ? n : sa::kSplitAuto;
 }
 
+// One device plan: its device copy, the pinned host copy it was uploaded
+// from (kept alive by the entry) and the event that marks the end of the
+// upload on the stream of the call that built it.
+struct Upload {
+    void* dev_base = nullptr;
+    void* host = nullptr;
+    hipEvent_t done = nullptr;
+    bool complete = false;
+    int device = 0;
+
+    // Make `stream` wait for the upload (a no-op once it has completed).
+    int order_after(void* stream) {
+        if (complete) return SA_OK;
+        const hipError_t q = hipEventQuery(done);
+        if (q == hipSuccess) {
+            complete = true;
+            return SA_OK;
+        }
+        if (q != hipErrorNotReady) return SA_ERR_HIP;
+        return hipStreamWaitEvent(static_cast<hipStream_t>(stream), done, 0) == hipSuccess ? SA_OK
+                                                                                            : SA_ERR_HIP;
+    }
+
+    void free_all() {
+        if (done) (void)hipEventDestroy(done);
+        if (host) (void)hipHostFree(host);
+        if (dev_base) (void)hipFree(dev_base);
+        done = nullptr;
+        host = nullptr;
+        dev_base = nullptr;
+    }
+};
+
+// Copy `bytes` of host plan data to a new device allocation, stream-ordered:
+// a pinned staging buffer, hipMemcpyAsync on `stream`, an event after it.
+int upload(const std::vector<unsigned char>& data, void* stream, int device, Upload* up) {
+    Upload u;
+    u.device = device;
+    const size_t bytes = data.size();
+    if (hipHostMalloc(&u.host, bytes, hipHostMallocDefault) != hipSuccess) {
+        (void)hipGetLastError();
+        return SA_ERR_NOMEM;
+    }
+    std::memcpy(u.host, data.data(), bytes);
+    if (hipMalloc(&u.dev_base, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        u.dev_base = nullptr;
+        u.free_all();
+        return SA_ERR_NOMEM;
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipEventCreateWithFlags(&u.done, hipEventDisableTiming) != hipSuccess ||
+        hipMemcpyAsync(u.dev_base, u.host, bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipEventRecord(u.done, s) != hipSuccess) {
+        (void)hipGetLastError();
+        // Nothing may still read the staging buffer once we free it.
+        (void)hipStreamSynchronize(s);
+        u.free_all();
+        return SA_ERR_HIP;
+    }
+    *up = u;
+    return SA_OK;
+}
+
 class PlanCache {
   public:
     // Returns SA_OK and a device plan for (spec, T, bq) on the current device;
-    // split_cap as build_plan's.
-    int get(const sa_mask& m, int T, int bq, int64_t split_cap, DevicePlan* out) {
+    // split_cap as build_plan's.  A plan built by this call is uploaded on
+    // `stream`; a plan built earlier on another stream is waited for.
+    int get(const sa_mask& m, int T, int bq, int64_t split_cap, void* stream, DevicePlan* out) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return SA_ERR_HIP;
         std::string key = sa::canonical_spec(m) + "|T=" + std::to_string(T) + "|bq=" +
@@ -66,7 +134,7 @@ class PlanCache {
         auto it = plans_.find(key);
         if (it != plans_.end()) {
             *out = it->second.plan;
-            return SA_OK;
+            return it->second.up.order_after(stream);
         }
         HostPlan hp = sa::build_plan(MaskRule(m, T), bq, sa::kBK, split_cap);
         DevicePlan dp;
@@ -111,21 +179,18 @@ class PlanCache {
         put(dp.off_item_part, hp.item_part.data(), hp.item_part.size() * 4);
         put(dp.off_split_qb, hp.split_qb.data(), hp.split_qb.size() * 4);
         put(dp.off_split_ptr, hp.split_ptr.data(), hp.split_ptr.size() * 4);
-        if (hipMalloc(&dp.base, dp.bytes) != hipSuccess) {
-            (void)hipGetLastError();
-            return SA_ERR_NOMEM;
-        }
-        if (hipMemcpy(dp.base, host.data(), dp.bytes, hipMemcpyHostToDevice) != hipSuccess) {
-            (void)hipFree(dp.base);
-            return SA_ERR_HIP;
-        }
-        plans_.emplace(key, Entry{dp, dev});
+        Upload up;
+        int rc = upload(host, stream, dev, &up);
+        if (rc != SA_OK) return rc;
+        dp.base = up.dev_base;
+        plans_.emplace(key, Entry{dp, up});
         *out = dp;
         return SA_OK;
     }
 
     // The backward plan (key blocks -> query tiles) for (spec, T).
-    int get_bwd(const sa_mask& m, int T, int bkb, int64_t split_cap, bool gather, sa::BwdDevicePlan* out) {
+    int get_bwd(const sa_mask& m, int T, int bkb, int64_t split_cap, bool gather, void* stream,
+                sa::BwdDevicePlan* out) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return SA_ERR_HIP;
         std::string key = sa::canonical_spec(m) + "|T=" + std::to_string(T) + "|bwd|bkb=" +
@@ -135,7 +200,7 @@ class PlanCache {
         auto it = bwd_.find(key);
         if (it != bwd_.end()) {
             *out = it->second.plan;
-            return SA_OK;
+            return it->second.up.order_after(stream);
         }
         sa::BwdHostPlan hp = sa::build_bwd_plan(MaskRule(m, T), bkb, split_cap, gather);
         sa::BwdDevicePlan dp;
@@ -170,15 +235,11 @@ class PlanCache {
         put(dp.off_item_part, hp.item_part.data(), hp.item_part.size() * 4);
         put(dp.off_split_kb, hp.split_kb.data(), hp.split_kb.size() * 4);
         put(dp.off_split_ptr, hp.split_ptr.data(), hp.split_ptr.size() * 4);
-        if (hipMalloc(&dp.base, dp.bytes) != hipSuccess) {
-            (void)hipGetLastError();
-            return SA_ERR_NOMEM;
-        }
-        if (hipMemcpy(dp.base, host.data(), dp.bytes, hipMemcpyHostToDevice) != hipSuccess) {
-            (void)hipFree(dp.base);
-            return SA_ERR_HIP;
-        }
-        bwd_.emplace(key, BwdEntry{dp, dev});
+        Upload up;
+        int rc = upload(host, stream, dev, &up);
+        if (rc != SA_OK) return rc;
+        dp.base = up.dev_base;
+        bwd_.emplace(key, BwdEntry{dp, up});
         *out = dp;
         return SA_OK;
     }
@@ -187,12 +248,10 @@ class PlanCache {
         std::lock_guard<std::mutex> lock(mu_);
         int cur = 0;
         bool have_cur = hipGetDevice(&cur) == hipSuccess;
-        for (auto& kv : plans_) {
-            if (hipSetDevice(kv.second.device) == hipSuccess) (void)hipFree(kv.second.plan.base);
-        }
-        for (auto& kv : bwd_) {
-            if (hipSetDevice(kv.second.device) == hipSuccess) (void)hipFree(kv.second.plan.base);
-        }
+        for (auto& kv : plans_)
+            if (hipSetDevice(kv.second.up.device) == hipSuccess) kv.second.up.free_all();
+        for (auto& kv : bwd_)
+            if (hipSetDevice(kv.second.up.device) == hipSuccess) kv.second.up.free_all();
         if (have_cur) (void)hipSetDevice(cur);
         plans_.clear();
         bwd_.clear();
@@ -201,11 +260,11 @@ class PlanCache {
   private:
     struct Entry {
         DevicePlan plan;
-        int device;
+        Upload up;
     };
     struct BwdEntry {
         sa::BwdDevicePlan plan;
-        int device;
+        Upload up;
     };
     std::mutex mu_;
     std::unordered_map<std::string, Entry> plans_;
@@ -217,34 +276,50 @@ PlanCache& cache() {
     return *c;
 }
 
-// fp32 scratch for the key-split partials of decode, one buffer per (device,
-// stream) so that calls on different streams never share one.  A buffer only
-// grows; growing waits for the device first, since work queued earlier may
-// still read the old buffer.
+// fp32 scratch (split partials, the backward's row dots, decode's key-split
+// partials), one buffer per (device, stream).  hipStreamPerThread names a
+// different stream in every host thread, so its buffers are also keyed by
+// thread.  A buffer only grows; before the old one is freed, the one stream
+// that uses it is synchronised (work queued on it may still read it).  The
+// caller holds the entry's lock from get() until its launches are enqueued,
+// so two host threads that share a stream cannot free a buffer under each
+// other.
 class Workspace {
   public:
-    int get(size_t bytes, void* stream, float** out) {
+    int get(size_t bytes, void* stream, float** out, std::unique_lock<std::mutex>* hold) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return SA_ERR_HIP;
-        const std::string key = std::to_string(dev) + "/" +
-                                std::to_string(reinterpret_cast<uintptr_t>(stream));
-        std::lock_guard<std::mutex> lock(mu_);
-        Entry& e = bufs_[key];
-        e.device = dev;
-        if (e.bytes < bytes) {
-            if (e.base) {
-                if (hipDeviceSynchronize() != hipSuccess) return SA_ERR_HIP;
-                (void)hipFree(e.base);
-                e.base = nullptr;
-                e.bytes = 0;
+        std::string key = std::to_string(dev) + "/" + std::to_string(reinterpret_cast<uintptr_t>(stream));
+        if (static_cast<hipStream_t>(stream) == hipStreamPerThread) {
+            std::ostringstream tid;
+            tid << std::this_thread::get_id();
+            key += "/" + tid.str();
+        }
+        Entry* e = nullptr;
+        {
+            std::lock_guard<std::mutex> lock(mu_);
+            std::unique_ptr<Entry>& slot = bufs_[key];
+            if (!slot) slot.reset(new Entry());
+            e = slot.get();
+        }
+        std::unique_lock<std::mutex> lk(e->mu);
+        e->device = dev;
+        if (e->bytes < bytes) {
+            if (e->base) {
+                if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return SA_ERR_HIP;
+                (void)hipFree(e->base);
+                e->base = nullptr;
+                e->bytes = 0;
             }
-            if (hipMalloc(&e.base, bytes) != hipSuccess) {
+            if (hipMalloc(&e->base, bytes) != hipSuccess) {
                 (void)hipGetLastError();
+                e->base = nullptr;
                 return SA_ERR_NOMEM;
             }
-            e.bytes = bytes;
+            e->bytes = bytes;
         }
-        *out = static_cast<float*>(e.base);
+        *out = static_cast<float*>(e->base);
+        *hold = std::move(lk);
         return SA_OK;
     }
 
@@ -252,21 +327,25 @@ class Workspace {
         std::lock_guard<std::mutex> lock(mu_);
         int cur = 0;
         bool have_cur = hipGetDevice(&cur) == hipSuccess;
-        for (auto& kv : bufs_)
-            if (kv.second.base && hipSetDevice(kv.second.device) == hipSuccess)
-                (void)hipFree(kv.second.base);
+        for (auto& kv : bufs_) {
+            std::lock_guard<std::mutex> lk(kv.second->mu);
+            if (kv.second->base && hipSetDevice(kv.second->device) == hipSuccess)
+                (void)hipFree(kv.second->base);
+            kv.second->base = nullptr;
+            kv.second->bytes = 0;
+        }
         if (have_cur) (void)hipSetDevice(cur);
-        bufs_.clear();
     }
 
   private:
     struct Entry {
+        std::mutex mu;
         void* base = nullptr;
         size_t bytes = 0;
         int device = 0;
     };
     std::mutex mu_;
-    std::unordered_map<std::string, Entry> bufs_;
+    std::unordered_map<std::string, std::unique_ptr<Entry>> bufs_;
 };
 
 Workspace& workspace() {
@@ -311,13 +390,13 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     // merge kernel).
     const bool fast = sa::fwd_fast_path(dtype, d, bq, sub);
     DevicePlan dp;
-    rc = cache().get(m, Ts, bq, fast && sub == 1 ? split_cap() : 0, &dp);
+    rc = cache().get(m, Ts, bq, fast && sub == 1 ? split_cap() : 0, stream, &dp);
     if (rc != SA_OK) return rc;
     // Partial slots grow with B*H: past kMaxSplitWorkspace the unsplit plan
     // runs instead (slower on blocks of global rows, same result).
     const size_t pbytes = size_t(BH) * size_t(dp.n_parts) * bq * (size_t(d) + 2) * sizeof(float);
     if (dp.n_parts > 0 && pbytes > kMaxSplitWorkspace) {
-        rc = cache().get(m, Ts, bq, 0, &dp);
+        rc = cache().get(m, Ts, bq, 0, stream, &dp);
         if (rc != SA_OK) return rc;
     }
     if (BH * sub * int64_t(dp.n_items) > INT32_MAX) return SA_ERR_SHAPE;
@@ -354,8 +433,9 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     a.item_part = dp.n_parts > 0 ? reinterpret_cast<const int32_t*>(base + dp.off_item_part) : nullptr;
     a.part = nullptr;
     a.n_parts = dp.n_parts;
+    std::unique_lock<std::mutex> ws_hold;
     if (dp.n_parts > 0) {
-        rc = workspace().get(pbytes, stream, &a.part);
+        rc = workspace().get(pbytes, stream, &a.part, &ws_hold);
         if (rc != SA_OK) return rc;
     }
     const int64_t grid = int64_t(a.BH) * dp.n_items;
@@ -406,10 +486,10 @@ int backward(int dtype, const void* Q, const void* K, const void* V, const void*
     const bool dma = dtype == SA_DTYPE_BF16 && (d == 64 || d == 128);
     const int64_t cap = dma ? split_cap() : 0;
     DevicePlan dp;
-    rc = cache().get(m, T, bq, cap, &dp);
+    rc = cache().get(m, T, bq, cap, stream, &dp);
     if (rc != SA_OK) return rc;
     sa::BwdDevicePlan bp;
-    rc = cache().get_bwd(m, T, bkb, cap, dma, &bp);
+    rc = cache().get_bwd(m, T, bkb, cap, dma, stream, &bp);
     if (rc != SA_OK) return rc;
     // Workspace: row dots D_i, then dQ partials, then dK and dV partials
     // (each section 256-byte aligned).  Past kMaxSplitWorkspace of partials
@@ -425,13 +505,14 @@ int backward(int dtype, const void* Q, const void* K, const void* V, const void*
     size_t q_off = 0, kv_off = 0;
     size_t wbytes = sized(dp, bp, &q_off, &kv_off);
     if (wbytes - align_up(lbytes, 256) > kMaxSplitWorkspace) {
-        rc = cache().get(m, T, bq, 0, &dp);
-        if (rc == SA_OK) rc = cache().get_bwd(m, T, bkb, 0, dma, &bp);
+        rc = cache().get(m, T, bq, 0, stream, &dp);
+        if (rc == SA_OK) rc = cache().get_bwd(m, T, bkb, 0, dma, stream, &bp);
         if (rc != SA_OK) return rc;
         wbytes = sized(dp, bp, &q_off, &kv_off);
     }
     float* Dw = nullptr;
-    rc = workspace().get(wbytes, stream, &Dw);
+    std::unique_lock<std::mutex> ws_hold;
+    rc = workspace().get(wbytes, stream, &Dw, &ws_hold);
     if (rc != SA_OK) return rc;
 
     sa::BwdArgs b;
@@ -572,9 +653,10 @@ int decode(const void* Q, const void* K, const void* V, void* O, const int32_t* 
     int64_t nsplit = (2048 + groups - 1) / groups;
     nsplit = std::max<int64_t>(1, std::min<int64_t>(nsplit, (keys + 255) / 256));
     a.nsplit = static_cast<int32_t>(nsplit);
+    std::unique_lock<std::mutex> ws_hold;
     if (a.nsplit > 1) {
         const size_t bytes = size_t(B) * H * n_new * size_t(a.nsplit) * (d + 2) * sizeof(float);
-        rc = workspace().get(bytes, stream, &a.part);
+        rc = workspace().get(bytes, stream, &a.part, &ws_hold);
         if (rc != SA_OK) return rc;
     }
     return sa::launch_decode(d, a, stream);
@@ -665,13 +747,23 @@ SA_EXPORT int sparse_attn_tile_map(const char* mask_spec, int T, int bq, int bk,
     });
 }
 
-SA_EXPORT int sparse_attn_tile_shape(int d, int dtype, int* bq, int* bk) {
-    if (!bq || !bk) return SA_ERR_NULL;
-    if (!supported_d(d) || (dtype != SA_DTYPE_BF16 && dtype != SA_DTYPE_F32))
-        return SA_ERR_UNSUPPORTED;
-    *bq = sa::kBQ;
-    *bk = sa::kBK;
-    return SA_OK;
+SA_EXPORT int sparse_attn_tile_shape(const char* mask_spec, int d, int dtype, int* bq, int* bk) {
+    return guarded([&] {
+        if (!bq || !bk) return SA_ERR_NULL;
+        if (!supported_d(d) || (dtype != SA_DTYPE_BF16 && dtype != SA_DTYPE_F32))
+            return SA_ERR_UNSUPPORTED;
+        sa_mask m;
+        std::memset(&m, 0, sizeof(m));
+        if (mask_spec) {
+            int rc = sa::parse_mask_spec(mask_spec, &m);
+            if (rc != SA_OK) return rc;
+        }
+        // The same choice the forward makes (a residue split keeps the
+        // plain window's tiles).
+        *bq = sa::fwd_query_block(m, d, dtype);
+        *bk = sa::kBK;
+        return SA_OK;
+    });
 }
 
 SA_EXPORT int sparse_attn_plan_info(const char* mask_spec, int T, int d, int dtype,
@@ -679,7 +771,7 @@ SA_EXPORT int sparse_attn_plan_info(const char* mask_spec, int T, int d, int dty
     return guarded([&] {
         if (!info) return SA_ERR_NULL;
         int bq = 0, bk = 0;
-        int rc = sparse_attn_tile_shape(d, dtype, &bq, &bk);
+        int rc = sparse_attn_tile_shape(mask_spec, d, dtype, &bq, &bk);
         if (rc != SA_OK) return rc;
         sa_mask m;
         rc = parse_for(mask_spec, T, &m);
@@ -690,7 +782,6 @@ SA_EXPORT int sparse_attn_plan_info(const char* mask_spec, int T, int d, int dty
         sa_mask mp = m;
         if (sub > 1) mp.dilation = 1;
         MaskRule prule(mp, T / sub);
-        bq = sa::fwd_query_block(mp, d, dtype);
         HostPlan hp = sa::build_plan(prule, bq, bk,
                                      sub == 1 && sa::fwd_fast_path(dtype, d, bq, sub) ? split_cap() : 0);
         std::memset(info, 0, sizeof(*info));
@@ -716,7 +807,7 @@ SA_EXPORT const char* sparse_attn_strerror(int status) {
     switch (status) {
         case SA_OK: return "ok";
         case SA_ERR_SPEC: return "mask spec does not parse";
-        case SA_ERR_RANGE: return "a global index is not below T";
+        case SA_ERR_RANGE: return "a global index is not below T, or phase is not below stride";
         case SA_ERR_SHAPE: return "bad shape (B, H or T < 1, T too large, or bad tile shape)";
         case SA_ERR_UNSUPPORTED: return "unsupported head dim or dtype (d must be 16, 32, 64 or 128)";
         case SA_ERR_NULL: return "a required pointer is NULL";

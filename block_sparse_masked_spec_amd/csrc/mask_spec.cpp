@@ -152,7 +152,7 @@ int parse_mask_spec(const char* text, sa_mask* out) {
         m.has_radius = 1;  // radius counts blocks; absent = 0 (the query's own block)
     }
     if (seen_phase && m.stride == 0) return SA_ERR_SPEC;
-    if (m.stride > 0 && m.phase >= m.stride) return SA_ERR_SPEC;
+    if (m.stride > 0 && m.phase >= m.stride) return SA_ERR_RANGE;  // well-formed, out of range
 
     // Sort and merge overlapping or touching ranges.
     std::sort(ranges.begin(), ranges.end());

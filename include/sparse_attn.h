@@ -47,7 +47,8 @@
  *           | 'radius=' INT        bidir only; absent = unlimited
  *           | 'dilation=' INT      >= 1; local keys sit this far apart
  *           | 'stride=' INT        0 = no strided columns
- *           | 'phase='  INT        needs stride > 0; 0 <= phase < stride
+ *           | 'phase='  INT        needs stride > 0 (else SA_ERR_SPEC);
+ *                                  0 <= phase < stride (else SA_ERR_RANGE)
  *           | 'global=' R (',' R)* R := INT | INT ':' INT  (half-open, a < b)
  *   bclause := 'radius=' INT       in blocks; default 0 (own block)
  *           | 'random=' INT        random key blocks per query block, <= 4096
@@ -69,7 +70,9 @@
  * grown on demand: partial results when a plan splits a heavy block (bf16
  * forward and backward; at most 1 GiB, past that the unsplit plan runs),
  * the backward's row dots and decode's key-split partials.  Calls are
- * thread-safe; calls that share a stream use its workspace in stream order.
+ * thread-safe; calls that share a stream use its workspace in stream order
+ * (hipStreamPerThread has one workspace per host thread, since it names a
+ * different stream in each).
  *
  * Tuning.  SA_FWD_SPLIT_TILES=n (n > 0) in the environment makes the bf16
  * d = 64 / 128 forward and backward split every query block (and, in the
@@ -79,8 +82,12 @@
  *
  * Streams.  Device work is enqueued on `stream` (a hipStream_t; NULL = the
  * null stream) of the current device; the call returns after the enqueue.
- * O is valid once the stream reaches that point.  Building a new plan makes
- * one synchronous host-to-device copy before the launch.
+ * O is valid once the stream reaches that point.  A new plan is uploaded
+ * with hipMemcpyAsync on the caller's stream from a pinned host buffer that
+ * the plan cache keeps alive; a call on another stream that finds the plan
+ * still in flight makes its stream wait for the upload (an event), so no
+ * call blocks the host or the device.  Growing a workspace synchronises
+ * only the stream that owns it (the old buffer may still be in use there).
  *
  * Errors.  Every call returns SA_OK or a negative status.  All checks run
  * before anything is enqueued, so on error O is untouched.  No C++
@@ -98,7 +105,7 @@ extern "C" {
 /* status codes */
 #define SA_OK 0
 #define SA_ERR_SPEC (-1)        /* mask spec does not parse */
-#define SA_ERR_RANGE (-2)       /* a global index >= T */
+#define SA_ERR_RANGE (-2)       /* a global index >= T, or phase >= stride */
 #define SA_ERR_SHAPE (-3)       /* B, H or T < 1, T > SA_MAX_T, bad tile shape */
 #define SA_ERR_UNSUPPORTED (-4) /* d not in {16, 32, 64, 128}, unknown dtype */
 #define SA_ERR_NULL (-5)        /* a required pointer is NULL */
@@ -213,7 +220,7 @@ int sparse_attn_bwd_f32(const void* Q, const void* K, const void* V, const void*
                         int H, int T, int d, const char* mask_spec, void* stream);
 
 /* Parse mask_spec into *out (host only).  SA_ERR_SPEC on any grammar
- * error, SA_ERR_NULL on NULL arguments. */
+ * error, SA_ERR_RANGE for phase >= stride, SA_ERR_NULL on NULL arguments. */
 int sparse_attn_parse(const char* mask_spec, sa_mask* out);
 
 /*
@@ -235,8 +242,14 @@ int sparse_attn_count(const char* mask_spec, int T, int64_t* allowed_cells,
 int sparse_attn_tile_map(const char* mask_spec, int T, int bq, int bk,
                          uint8_t* map);
 
-/* The tile shape the kernel uses for head dim d and dtype (SA_DTYPE_*). */
-int sparse_attn_tile_shape(int d, int dtype, int* bq, int* bk);
+/* The tile shape (query rows bq x keys bk) the forward kernel uses for
+ * mask_spec, head dim d and dtype (SA_DTYPE_*); the same shape that
+ * sparse_attn_plan_info reports.  mask_spec may be NULL: the shape of the
+ * token-level specs (causal / bidir), 128 x 64.  Block mode with a block
+ * size that is a multiple of 64 but not of 128 runs 64 x 64 tiles at bf16,
+ * d = 64 (every tile then lies in one query block).  Host only.  Returns
+ * SA_OK or SA_ERR_{NULL, UNSUPPORTED, SPEC, RANGE}. */
+int sparse_attn_tile_shape(const char* mask_spec, int d, int dtype, int* bq, int* bk);
 
 /* Describe the plan the kernel would run (host only; builds no device
  * state). */

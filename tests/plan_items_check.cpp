@@ -221,6 +221,50 @@ int check_bwd(const std::string& spec, int T, int bkb, int64_t cap, bool gather)
     return 0;
 }
 
+// Parser robustness: random strings over the grammar's alphabet and single-
+// character mutations of valid specs must parse to SA_OK, SA_ERR_SPEC or
+// SA_ERR_RANGE (never crash or read out of bounds -- the sanitizer build of
+// this program checks that); a spec that parses must survive the round trip
+// through its canonical text unchanged.
+int fuzz_parser(Lcg& r, int n) {
+    static const char alphabet[] = "causlbidrwnophetgkzfm=;:,0123456789 -x";
+    const char* seeds[] = {"causal;window=4096", "bidir;radius=256;stride=16;phase=0;global=0:128",
+                           "blocks;block=64;radius=1;random=3;seed=0;global=0:128",
+                           "causal;window=9;dilation=2;stride=5;phase=4;global=3,7:9"};
+    for (int c = 0; c < n; ++c) {
+        std::string s;
+        if (c % 2) {
+            const int len = r.below(60);
+            for (int k = 0; k < len; ++k) s += alphabet[r.below(int(sizeof(alphabet)) - 1)];
+        } else {
+            s = seeds[r.below(4)];
+            const int edits = 1 + r.below(3);
+            for (int e = 0; e < edits && !s.empty(); ++e) {
+                const int at = r.below(int(s.size()));
+                switch (r.below(3)) {
+                    case 0: s[at] = alphabet[r.below(int(sizeof(alphabet)) - 1)]; break;
+                    case 1: s.erase(at, 1); break;
+                    default: s.insert(s.begin() + at, alphabet[r.below(int(sizeof(alphabet)) - 1)]);
+                }
+            }
+        }
+        sa_mask m;
+        const int rc = sa::parse_mask_spec(s.c_str(), &m);
+        if (rc != SA_OK && rc != SA_ERR_SPEC && rc != SA_ERR_RANGE) {
+            std::printf("parser: status %d for \"%s\"\n", rc, s.c_str());
+            return 1;
+        }
+        if (rc != SA_OK) continue;
+        sa_mask back;
+        const std::string canon = sa::canonical_spec(m);
+        if (sa::parse_mask_spec(canon.c_str(), &back) != SA_OK || sa::canonical_spec(back) != canon) {
+            std::printf("parser: round trip of \"%s\" via \"%s\"\n", s.c_str(), canon.c_str());
+            return 1;
+        }
+    }
+    return 0;
+}
+
 }  // namespace
 
 int main() {
@@ -251,6 +295,7 @@ int main() {
         if (check_bwd(spec, T, bq == 64 ? 64 : 128, cap, true)) return 1;
         cases += 3;
     }
+    if (fuzz_parser(r, 20000)) return 1;
     std::printf("ok %d\n", cases);
     return 0;
 }

@@ -355,3 +355,82 @@ def test_plan_cache_release_and_rebuild(gpu):
     gpu.sparse_attn_release_cache()
     b = run_gpu(gpu, "causal;window=33;stride=8", q, k, v)
     assert torch.equal(a, b)
+
+
+def test_plan_built_on_one_stream_used_on_another(gpu):
+    """A new plan is uploaded asynchronously on the stream of the call that
+    builds it; a call on a second stream, enqueued before the first has
+    run, waits for that upload (event) instead of reading a half-written
+    plan."""
+    spec = "causal;window=77;stride=13;phase=2;global=40:45"
+    gpu.sparse_attn_release_cache()
+    q, k, v = inputs.qkv(2, 3, 700, 128, "bf16", 21)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o1, o2 = torch.empty_like(qd), torch.empty_like(qd)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    announce(f"fwd two streams spec={spec}")
+    gpu.sparse_attn_fwd(qd, kd, vd, o1, 2, 3, 700, 128, spec, s1)
+    gpu.sparse_attn_fwd(qd, kd, vd, o2, 2, 3, 700, 128, spec, s2)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.forward_rows(spec, q, k, v)
+    check_bf16(o1.cpu(), ref, "stream 1")
+    check_bf16(o2.cpu(), ref, "stream 2")
+
+
+def test_workspace_growth_on_a_busy_stream(gpu, monkeypatch):
+    """Split plans need partial slots in the stream's workspace; a second
+    call that needs a larger one is enqueued while the first may still run
+    (the old buffer is freed only after that stream has drained)."""
+    monkeypatch.setenv("SA_FWD_SPLIT_TILES", "1")
+    spec = "bidir;radius=40;stride=16;global=0:8"
+    gpu.sparse_attn_release_cache()
+    s = torch.cuda.Stream()
+    outs = []
+    for (B, H, T, seed) in [(1, 1, 300, 1), (2, 4, 900, 2), (2, 8, 1000, 3)]:
+        q, k, v = inputs.qkv(B, H, T, 64, "bf16", seed)
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        od = torch.empty_like(qd)
+        announce(f"fwd split on one stream B={B} H={H} T={T}")
+        gpu.sparse_attn_fwd(qd, kd, vd, od, B, H, T, 64, spec, s)
+        outs.append((q, k, v, od, (qd, kd, vd)))
+    torch.cuda.synchronize()
+    for q, k, v, od, _ in outs:
+        ref, _, _ = oracle.forward_rows(spec, q, k, v)
+        check_bf16(od.cpu(), ref, f"T={q.shape[2]}")
+
+
+def test_per_thread_default_stream_from_several_threads(gpu, monkeypatch):
+    """hipStreamPerThread names a different stream in every host thread, so
+    each thread gets its own workspace for split partials; four threads
+    call the split forward at once and every result matches the oracle."""
+    import threading
+    monkeypatch.setenv("SA_FWD_SPLIT_TILES", "2")
+    spec = "bidir;radius=64;stride=16;phase=0;global=0:128"
+    per_thread = 2  # hipStreamPerThread
+    cases = [inputs.qkv(1, 2 + t, 600 + 100 * t, 64, "bf16", 30 + t) for t in range(4)]
+    dev = [tuple(x.cuda() for x in c) for c in cases]
+    outs = [torch.empty_like(d[0]) for d in dev]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(t):
+        try:
+            q, k, v = dev[t]
+            B, H, T, d = q.shape
+            for _ in range(3):
+                gpu.sparse_attn_fwd(q, k, v, outs[t], B, H, T, d, spec, per_thread)
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(e)
+
+    announce(f"fwd from 4 threads on hipStreamPerThread spec={spec}")
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for t, (q, k, v) in enumerate(cases):
+        ref, _, _ = oracle.forward_rows(spec, q, k, v)
+        check_bf16(outs[t].cpu(), ref, f"thread {t}")

@@ -122,7 +122,7 @@ def test_plan_info_struct_size_matches_header():
 # ------------------------------------------------------------------- parser
 @pytest.mark.parametrize("bad", [
     "", "sparse", "causal;radius=3", "bidir;window=3", "causal;window=3;window=4",
-    "causal;phase=1", "causal;stride=4;phase=4", "causal;window=-1", "causal;foo=1",
+    "causal;phase=1", "causal;window=-1", "causal;foo=1",
     "bidir;global=5:5", "bidir;global=a", "causal;window", "causal;stride=4;phase=x",
     "causal;window=99999999999", "causal;;window=2", "causal;window=2;", "causal window=2",
     "causal;dilation=0", "causal;window=4;dilation=2;dilation=3", "bidir;dilation=",
@@ -136,6 +136,46 @@ def test_parser_rejects(bad):
     assert e.value.status == sa.SA_ERR_SPEC
     with pytest.raises(oracle.OracleSpecError):  # the oracle's own parser agrees
         oracle.parse_spec(bad)
+
+
+@pytest.mark.parametrize("spec", ["causal;stride=4;phase=4", "bidir;radius=2;stride=16;phase=99",
+                                  "blocks;block=8;stride=3;phase=3"])
+def test_parser_phase_not_below_stride_is_a_range_error(spec):
+    """A well-formed phase that is not below the stride is out of range
+    (SA_ERR_RANGE, not a grammar error); the oracle's parser rejects it too."""
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_parse(spec)
+    assert e.value.status == sa.SA_ERR_RANGE
+    with pytest.raises(oracle.OracleSpecError):
+        oracle.parse_spec(spec)
+    lib = sa.load()
+    v = ctypes.c_int64(0)
+    assert lib.sparse_attn_count(spec.encode(), 64, ctypes.byref(v), None) == sa.SA_ERR_RANGE
+    assert lib.sparse_attn_fwd(0x10000, 0x20000, 0x30000, 0x40000, 1, 1, 16, 16, spec.encode(),
+                               None) == sa.SA_ERR_RANGE
+
+
+def test_tile_shape_agrees_with_plan_info():
+    """The tile shape answered for a spec is the one the forward's plan uses:
+    64 x 64 for block mode with 64-key blocks at bf16 d = 64, else 128 x 64."""
+    cases = [
+        ("causal;window=4096", 128, sa.SA_DTYPE_BF16, (128, 64)),
+        ("bidir;radius=256;stride=16;phase=0;global=0:128", 64, sa.SA_DTYPE_BF16, (128, 64)),
+        ("blocks;block=64;radius=1;random=3;seed=0;global=0:128", 64, sa.SA_DTYPE_BF16, (64, 64)),
+        ("blocks;block=64;radius=1;random=3", 64, sa.SA_DTYPE_F32, (128, 64)),
+        ("blocks;block=64;radius=1;random=3", 128, sa.SA_DTYPE_BF16, (128, 64)),
+        ("blocks;block=128;radius=1", 64, sa.SA_DTYPE_BF16, (128, 64)),
+        ("causal;window=8;dilation=2", 64, sa.SA_DTYPE_BF16, (128, 64)),
+    ]
+    for spec, d, dt, want in cases:
+        got = sa.sparse_attn_tile_shape(spec, d, dt)
+        assert got == want, (spec, d, dt, got)
+        info = sa.sparse_attn_plan_info(spec, 1000, d, dt)
+        assert (info["bq"], info["bk"]) == got, spec
+    assert sa.sparse_attn_tile_shape(None, 128) == (128, 64)
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_tile_shape("causal;window=x", 64)
+    assert e.value.status == sa.SA_ERR_SPEC
 
 
 def test_parser_fields_and_normalisation():
@@ -197,7 +237,7 @@ def test_tile_maps_match_oracle_on_random_specs():
 
 @pytest.mark.parametrize("spec,T", CONFIG_SPECS[:6] + CONFIG_SPECS[8:])
 def test_tile_maps_match_oracle_on_config_specs(spec, T):
-    bq, bk = sa.sparse_attn_tile_shape(64)
+    bq, bk = sa.sparse_attn_tile_shape(spec, 64)
     assert np.array_equal(sa.sparse_attn_tile_map(spec, T, bq, bk), oracle.tile_map(spec, T, bq, bk))
 
 
@@ -205,7 +245,7 @@ def test_tile_map_32k_window_class_counts():
     """The 32768-token window-4096 grid at the kernel's tile shape, against the
     oracle's full pair scan (about 1e9 pair evaluations)."""
     spec, T = "causal;window=4096", 32768
-    bq, bk = sa.sparse_attn_tile_shape(128)
+    bq, bk = sa.sparse_attn_tile_shape(spec, 128)
     mine = sa.sparse_attn_tile_map(spec, T, bq, bk)
     ref = oracle.tile_map(spec, T, bq, bk)
     assert np.array_equal(mine, ref)
@@ -254,7 +294,7 @@ def test_random_specs_counts_and_tile_maps(chunk):
         ref_total, ref_rows = oracle.count(spec, T, per_row=True)
         assert total == ref_total, spec
         assert np.array_equal(rows.astype(np.int64), ref_rows), spec
-        bq, bk = sa.sparse_attn_tile_shape(64)
+        bq, bk = sa.sparse_attn_tile_shape(spec, 64)
         assert np.array_equal(sa.sparse_attn_tile_map(spec, T, bq, bk), oracle.tile_map(spec, T, bq, bk)), spec
 
 
@@ -325,8 +365,11 @@ def test_count_and_map_errors():
     assert lib.sparse_attn_tile_map(b"causal", 16, 0, 4, buf) == sa.SA_ERR_SHAPE
     assert lib.sparse_attn_tile_map(b"causal", 16, 4, 4, None) == sa.SA_ERR_NULL
     bq, bk = ctypes.c_int(0), ctypes.c_int(0)
-    assert lib.sparse_attn_tile_shape(48, 0, ctypes.byref(bq), ctypes.byref(bk)) == sa.SA_ERR_UNSUPPORTED
-    assert lib.sparse_attn_tile_shape(64, 7, ctypes.byref(bq), ctypes.byref(bk)) == sa.SA_ERR_UNSUPPORTED
+    assert lib.sparse_attn_tile_shape(None, 48, 0, ctypes.byref(bq), ctypes.byref(bk)) == sa.SA_ERR_UNSUPPORTED
+    assert lib.sparse_attn_tile_shape(b"causal", 64, 7, ctypes.byref(bq), ctypes.byref(bk)) == sa.SA_ERR_UNSUPPORTED
+    assert lib.sparse_attn_tile_shape(b"causal", 64, 0, None, ctypes.byref(bk)) == sa.SA_ERR_NULL
+    assert lib.sparse_attn_tile_shape(b"causal;stride=2;phase=2", 64, 0, ctypes.byref(bq),
+                                      ctypes.byref(bk)) == sa.SA_ERR_RANGE
 
 
 def test_forward_rejects_bad_arguments_before_any_device_work():

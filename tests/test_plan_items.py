@@ -19,14 +19,34 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "..", "block_sparse_masked_spec_amd", "csrc")
 
 
+SOURCES = [os.path.join(HERE, "plan_items_check.cpp"), os.path.join(CSRC, "plan.cpp"),
+           os.path.join(CSRC, "mask_spec.cpp")]
+
+
+def build_and_run(tmp_path, name, flags, env=None):
+    exe = str(tmp_path / name)
+    build = subprocess.run(["g++", "-std=c++20", "-Wall", *flags, "-o", exe, *SOURCES],
+                           capture_output=True, text=True, timeout=600)
+    assert build.returncode == 0, build.stderr[-2000:]
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=600,
+                         env={**os.environ, **(env or {})})
+    assert run.returncode == 0 and run.stdout.startswith("ok"), run.stdout[-2000:] + run.stderr[-4000:]
+    assert int(run.stdout.split()[1]) >= 1200
+
+
 @pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
 def test_split_items_cover_each_block_exactly(tmp_path):
-    exe = str(tmp_path / "plan_items_check")
-    build = subprocess.run(
-        ["g++", "-std=c++20", "-O1", "-Wall", "-o", exe, os.path.join(HERE, "plan_items_check.cpp"),
-         os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "mask_spec.cpp")],
-        capture_output=True, text=True, timeout=300)
-    assert build.returncode == 0, build.stderr[-2000:]
-    run = subprocess.run([exe], capture_output=True, text=True, timeout=300)
-    assert run.returncode == 0 and run.stdout.startswith("ok"), run.stdout[-2000:] + run.stderr[-2000:]
-    assert int(run.stdout.split()[1]) >= 1200
+    build_and_run(tmp_path, "plan_items_check", ["-O1"])
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_parser_and_planner_under_address_and_ub_sanitizers(tmp_path):
+    """The same program (plan coverage plus 20000 fuzzed specs through the
+    parser) built with AddressSanitizer and UndefinedBehaviorSanitizer on the
+    host: any out-of-bounds access, leak, overflow or other undefined
+    behaviour in the parser or planner aborts it."""
+    build_and_run(tmp_path, "plan_items_check_asan",
+                  ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                   "-fno-sanitize-recover=undefined"],
+                  env={"ASAN_OPTIONS": "detect_leaks=1:abort_on_error=0",
+                       "UBSAN_OPTIONS": "print_stacktrace=1:halt_on_error=1"})
