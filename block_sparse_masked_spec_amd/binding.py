@@ -30,6 +30,8 @@ SA_ERR_ALIAS = -6
 SA_ERR_HIP = -7
 SA_ERR_ALIGN = -8
 SA_ERR_NOMEM = -9
+SA_ERR_SCRATCH = -10
+SA_DECODE_SCRATCH_BYTES = 16 << 20
 
 SA_TILE_EMPTY, SA_TILE_FULL, SA_TILE_PARTIAL = 0, 1, 2
 SA_DTYPE_BF16, SA_DTYPE_F32 = 0, 1
@@ -40,7 +42,7 @@ EXPORTED = [
     "sparse_attn_tile_map", "sparse_attn_tile_shape", "sparse_attn_plan_info",
     "sparse_attn_strerror", "sparse_attn_release_cache", "sparse_attn_decode",
     "sparse_attn_decode_cache_rows", "sparse_attn_fwd_lse", "sparse_attn_fwd_lse_f32",
-    "sparse_attn_bwd", "sparse_attn_bwd_f32",
+    "sparse_attn_bwd", "sparse_attn_bwd_f32", "sparse_attn_decode_noalloc",
 ]
 
 
@@ -115,6 +117,8 @@ def load():
     lib.sparse_attn_bwd_f32.restype = i32
     lib.sparse_attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, cs, vp]
     lib.sparse_attn_decode.restype = i32
+    lib.sparse_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, cs, vp]
+    lib.sparse_attn_decode_noalloc.restype = i32
     lib.sparse_attn_decode_cache_rows.argtypes = [cs, i32, ctypes.POINTER(i64)]
     lib.sparse_attn_decode_cache_rows.restype = i32
     lib.sparse_attn_release_cache.argtypes = []
@@ -246,6 +250,16 @@ def sparse_attn_decode(Q, K_cache, V_cache, O, pos, B, H, Hkv, n_new, C, d, mask
                                             _ptr(pos), B, H, Hkv, n_new, C, d, _spec(mask_spec),
                                             _stream_handle(stream)),
                   "sparse_attn_decode")
+
+
+def sparse_attn_decode_noalloc(Q, K_cache, V_cache, O, pos, B, H, Hkv, n_new, C, d, mask_spec,
+                               stream=None):
+    """sparse_attn_decode with its partials in the library's static scratch
+    (allocates nothing); stream defaults to torch's current stream."""
+    return _check(load().sparse_attn_decode_noalloc(_ptr(Q), _ptr(K_cache), _ptr(V_cache), _ptr(O),
+                                                    _ptr(pos), B, H, Hkv, n_new, C, d,
+                                                    _spec(mask_spec), _stream_handle(stream)),
+                  "sparse_attn_decode_noalloc")
 
 
 def sparse_attn_decode_cache_rows(mask_spec, n_new=1) -> int:

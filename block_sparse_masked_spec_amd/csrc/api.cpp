@@ -605,8 +605,11 @@ int decode_mask(const char* spec, int n_new, sa_mask* m, int64_t* min_rows) {
     return SA_OK;
 }
 
-int decode(const void* Q, const void* K, const void* V, void* O, const int32_t* pos, int B,
-           int H, int Hkv, int n_new, int C, int d, const char* spec, void* stream) {
+// Validation and launch arguments of a decode call; *part_bytes receives the
+// size of the key-split partials the launch needs (0 with one split).
+int decode_prepare(const void* Q, const void* K, const void* V, void* O, const int32_t* pos,
+                   int B, int H, int Hkv, int n_new, int C, int d, const char* spec,
+                   sa::DecodeArgs* out, size_t* part_bytes) {
     if (!Q || !K || !V || !O || !pos || !spec) return SA_ERR_NULL;
     if (B < 1 || H < 1 || Hkv < 1 || n_new < 1 || C < 1 || C > SA_MAX_T || H % Hkv != 0 ||
         B > 65535)
@@ -629,7 +632,7 @@ int decode(const void* Q, const void* K, const void* V, void* O, const int32_t* 
         overlaps(O, qbytes, V, kvbytes))
         return SA_ERR_ALIAS;
 
-    sa::DecodeArgs a;
+    sa::DecodeArgs& a = *out;
     a.Q = Q;
     a.K = K;
     a.V = V;
@@ -653,10 +656,34 @@ int decode(const void* Q, const void* K, const void* V, void* O, const int32_t* 
     int64_t nsplit = (2048 + groups - 1) / groups;
     nsplit = std::max<int64_t>(1, std::min<int64_t>(nsplit, (keys + 255) / 256));
     a.nsplit = static_cast<int32_t>(nsplit);
+    *part_bytes = a.nsplit > 1 ? size_t(B) * H * n_new * size_t(a.nsplit) * (d + 2) * sizeof(float) : 0;
+    return SA_OK;
+}
+
+int decode(const void* Q, const void* K, const void* V, void* O, const int32_t* pos, int B,
+           int H, int Hkv, int n_new, int C, int d, const char* spec, void* stream) {
+    sa::DecodeArgs a;
+    size_t bytes = 0;
+    int rc = decode_prepare(Q, K, V, O, pos, B, H, Hkv, n_new, C, d, spec, &a, &bytes);
+    if (rc != SA_OK) return rc;
     std::unique_lock<std::mutex> ws_hold;
-    if (a.nsplit > 1) {
-        const size_t bytes = size_t(B) * H * n_new * size_t(a.nsplit) * (d + 2) * sizeof(float);
+    if (bytes > 0) {
         rc = workspace().get(bytes, stream, &a.part, &ws_hold);
+        if (rc != SA_OK) return rc;
+    }
+    return sa::launch_decode(d, a, stream);
+}
+
+// The same decode with the partials in the library's static per-device
+// scratch array: no allocation on any path.
+int decode_noalloc(const void* Q, const void* K, const void* V, void* O, const int32_t* pos,
+                   int B, int H, int Hkv, int n_new, int C, int d, const char* spec, void* stream) {
+    sa::DecodeArgs a;
+    size_t bytes = 0;
+    int rc = decode_prepare(Q, K, V, O, pos, B, H, Hkv, n_new, C, d, spec, &a, &bytes);
+    if (rc != SA_OK) return rc;
+    if (bytes > 0) {
+        rc = sa::decode_scratch(bytes, &a.part);
         if (rc != SA_OK) return rc;
     }
     return sa::launch_decode(d, a, stream);
@@ -815,6 +842,7 @@ SA_EXPORT const char* sparse_attn_strerror(int status) {
         case SA_ERR_HIP: return "HIP runtime or launch error";
         case SA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
         case SA_ERR_NOMEM: return "allocation failed";
+        case SA_ERR_SCRATCH: return "the call needs more than the static decode scratch holds";
         default: return "unknown status";
     }
 }
@@ -824,6 +852,15 @@ SA_EXPORT int sparse_attn_decode(const void* Q, const void* K_cache, const void*
                                  int d, const char* mask_spec, void* stream) {
     return guarded([&] {
         return decode(Q, K_cache, V_cache, O, pos, B, H, Hkv, n_new, C, d, mask_spec, stream);
+    });
+}
+
+SA_EXPORT int sparse_attn_decode_noalloc(const void* Q, const void* K_cache, const void* V_cache,
+                                         void* O, const int32_t* pos, int B, int H, int Hkv,
+                                         int n_new, int C, int d, const char* mask_spec,
+                                         void* stream) {
+    return guarded([&] {
+        return decode_noalloc(Q, K_cache, V_cache, O, pos, B, H, Hkv, n_new, C, d, mask_spec, stream);
     });
 }
 

@@ -26,10 +26,25 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "internal.hpp"
 
 namespace sa {
+
+// Scratch of the allocation-free decode entry point: the key-split partials
+// live in this file-scope device array instead of the library workspace.
+// Every GPU the library runs on holds its own copy until the process ends.
+// In host code the name `scratch` is only a stand-in for the symbol, never a
+// device address: the address (different on each GPU) comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+float* scratch_addr[kMaxDevices] = {};  // per device, filled on first use
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -333,6 +348,25 @@ int launch_dec_d(const DecodeArgs& a, void* stream) {
 }
 
 }  // namespace
+
+int decode_scratch(size_t bytes, float** out) {
+    if (bytes > kDecodeScratchBytes) return SA_ERR_SCRATCH;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return SA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_addr[dev]) {
+        // Once per device, with that device current.
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return SA_ERR_HIP;
+        }
+        scratch_addr[dev] = static_cast<float*>(p);
+    }
+    *out = scratch_addr[dev];
+    return SA_OK;
+}
 
 int launch_decode(int d, const DecodeArgs& a, void* stream) {
     switch (d) {

@@ -280,6 +280,13 @@ struct DecodeArgs {
 
 int launch_decode(int d, const DecodeArgs& args, void* stream);
 
+// Size of the static scratch array of the allocation-free decode entry point
+// (one per GPU, for the key-split partials).
+constexpr size_t kDecodeScratchBytes = size_t(SA_DECODE_SCRATCH_BYTES);
+// That array's device address on the current device (looked up once per
+// device); SA_ERR_SCRATCH when `bytes` exceeds kDecodeScratchBytes.
+int decode_scratch(size_t bytes, float** out);
+
 // A pure dilated window (no strided or global keys) links only rows of equal
 // residue mod g, and within a residue class it is the plain window.  When T
 // is a multiple of g the forward then runs as g interleaved plain-window

@@ -113,6 +113,8 @@ extern "C" {
 #define SA_ERR_HIP (-7)         /* a HIP runtime call or the launch failed */
 #define SA_ERR_ALIGN (-8)       /* a tensor pointer is not 16-byte aligned */
 #define SA_ERR_NOMEM (-9)       /* host or device allocation for a plan failed */
+#define SA_ERR_SCRATCH (-10)    /* sparse_attn_decode_noalloc: the call needs more
+                                   than the static scratch holds */
 
 /* tile classes written by sparse_attn_tile_map */
 #define SA_TILE_EMPTY 0   /* no allowed pair among the tile's in-range cells */
@@ -294,6 +296,38 @@ int sparse_attn_plan_info(const char* mask_spec, int T, int d, int dtype,
 int sparse_attn_decode(const void* Q, const void* K_cache, const void* V_cache, void* O,
                        const int32_t* pos, int B, int H, int Hkv, int n_new, int C, int d,
                        const char* mask_spec, void* stream);
+
+/*
+ * Allocation-free windowed decode, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Arguments, layout, semantics and errors are those of
+ * sparse_attn_decode, and the result is bit-identical to it (same kernels,
+ * same key splits).  The difference: the key-split partials live in a static
+ * device array of SA_DECODE_SCRATCH_BYTES per GPU (part of the library's
+ * device code, so each GPU it is loaded on holds one until the process
+ * ends), instead of the library workspace; no call on this path allocates or frees memory (hipMalloc,
+ * hipFree, host containers).  The array's address on a device is looked up
+ * on this entry point's first call on that device.
+ *
+ * A call needs B * H * n_new * nsplit * (d + 2) * 4 bytes of scratch when it
+ * splits the cache over nsplit > 1 workgroups (nsplit = ceil(2048 / groups)
+ * for groups = B * Hkv * ceil(H / Hkv * n_new / 8) below 2048, capped so each
+ * split covers at least 256 keys; one split needs none).  That is at most
+ * about 17 MB (d = 128, groups just below 2048); a call that needs more than
+ * SA_DECODE_SCRATCH_BYTES (16 MiB) returns SA_ERR_SCRATCH before any device
+ * work -- for example B = 255, H = 64, Hkv = 8, n_new = 1, d = 128 with a
+ * 4096-row window -- and can use sparse_attn_decode instead.  Every partial a call reads is written by the same call first, so
+ * nothing has to start at zero.
+ *
+ * All calls on one GPU share that GPU's array: calls on one stream are
+ * ordered, but calls that may overlap in time on one GPU (different streams,
+ * or several host threads without a common stream) race on it and must not
+ * be issued.
+ */
+#define SA_DECODE_SCRATCH_BYTES (16 << 20)
+int sparse_attn_decode_noalloc(const void* Q, const void* K_cache, const void* V_cache, void* O,
+                               const int32_t* pos, int B, int H, int Hkv, int n_new, int C,
+                               int d, const char* mask_spec, void* stream);
 
 /* Cache rows decode needs for mask_spec and n_new new tokens (host only):
  * (w-1)*g + n_new for a window w with dilation g -- for n_new = 1 and g = 1

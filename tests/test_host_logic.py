@@ -105,10 +105,14 @@ def test_library_exports_every_header_function():
 def test_header_status_codes_match_binding():
     text = open(HEADER).read()
     for name in ["SA_OK", "SA_ERR_SPEC", "SA_ERR_RANGE", "SA_ERR_SHAPE", "SA_ERR_UNSUPPORTED",
-                 "SA_ERR_NULL", "SA_ERR_ALIAS", "SA_ERR_HIP", "SA_ERR_ALIGN", "SA_ERR_NOMEM"]:
-        m = re.search(rf"#define {name} \(?(-?\d+)\)?", text)
-        assert m and int(m.group(1)) == getattr(sa, name), name
-        assert sa.strerror(getattr(sa, name)) != "unknown status"
+                 "SA_ERR_NULL", "SA_ERR_ALIAS", "SA_ERR_HIP", "SA_ERR_ALIGN", "SA_ERR_NOMEM",
+                 "SA_ERR_SCRATCH", "SA_DECODE_SCRATCH_BYTES"]:
+        m = re.search(rf"#define {name} \((-?\d+)(?: << (\d+))?\)|#define {name} (-?\d+)", text)
+        assert m, name
+        value = int(m.group(1)) << int(m.group(2) or 0) if m.group(1) else int(m.group(3))
+        assert value == getattr(sa, name), name
+        if name.startswith("SA_ERR") or name == "SA_OK":
+            assert sa.strerror(value) != "unknown status"
 
 
 def test_plan_info_struct_size_matches_header():
@@ -456,6 +460,24 @@ def test_decode_rejects_bad_arguments_before_any_device_work():
     assert call(Q=Q + 8) == sa.SA_ERR_ALIGN
     assert call(pos=P + 2) == sa.SA_ERR_ALIGN
     assert call(O=K + 64) == sa.SA_ERR_ALIAS
+
+
+def test_noalloc_decode_checks_before_any_device_work():
+    """The allocation-free decode validates like decode, and refuses a call
+    whose partials exceed its static scratch (SA_ERR_SCRATCH), all before
+    touching the device (the fake pointers are never read)."""
+    lib = sa.load()
+    Q, K, V, O, P = 0x10000, 0x1000000000, 0x2000000000, 0x600000, 0x800000
+    dec = lib.sparse_attn_decode_noalloc
+    w = b"causal;window=4096"
+    assert dec(None, K, V, O, P, 2, 8, 2, 1, 4096, 128, w, None) == sa.SA_ERR_NULL
+    assert dec(Q, K, V, O, P, 2, 8, 2, 1, 100, 128, w, None) == sa.SA_ERR_SHAPE
+    assert dec(Q, K, V, O, P, 2, 8, 2, 1, 4096, 48, w, None) == sa.SA_ERR_UNSUPPORTED
+    assert dec(Q, K, V, O, P, 2, 8, 2, 1, 4096, 128, b"causal;stride=4", None) == sa.SA_ERR_UNSUPPORTED
+    # 255 x 8 groups get 2 key splits: 255*64*2*130*4 = 16.97 MB > 16 MiB
+    assert 255 * 64 * 2 * 130 * 4 > sa.SA_DECODE_SCRATCH_BYTES
+    assert dec(Q, K, V, O, P, 255, 64, 8, 1, 4096, 128, w, None) == sa.SA_ERR_SCRATCH
+    assert sa.strerror(sa.SA_ERR_SCRATCH) != "unknown status"
 
 
 def test_backward_rejects_bad_arguments_before_any_device_work():
