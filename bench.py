@@ -32,6 +32,7 @@ METRIC = "allowed attention cells/s and effective TFLOP/s at 1 MI355X; % of bf16
 BF16_PEAK_TFLOPS = 2500.0
 F32_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
+VENDOR_SCLK_MHZ = 2400.0  # the clock the vendor's peak figures are quoted at
 CSRC = os.path.join(ROOT, "block_sparse_masked_spec_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -40,10 +41,17 @@ WORKLOADS = {
                                   specs=["causal;window=4096"]),
     "code_layer512_w128_s64": dict(B=8, H=8, T=512, d=64, dtype="bf16",
                                    specs=["causal;window=128;stride=64;phase=0"]),
+    "code_layer512_w128_s0": dict(B=8, H=8, T=512, d=64, dtype="bf16", specs=["causal;window=128"]),
+    "code_layer512_w256_s64": dict(B=8, H=8, T=512, d=64, dtype="bf16",
+                                   specs=["causal;window=256;stride=64;phase=0"]),
+    "code_layer512_w256_s0": dict(B=8, H=8, T=512, d=64, dtype="bf16", specs=["causal;window=256"]),
+    "code_layer512_full_causal": dict(B=8, H=8, T=512, d=64, dtype="bf16", specs=["causal"]),
     "longformer16k_r256_s16_g128": dict(B=1, H=16, T=16384, d=64, dtype="bf16",
                                         specs=["bidir;radius=256;stride=16;phase=0;global=0:128"]),
     "gemma_interleave_8k": dict(B=2, H=16, T=8192, d=128, dtype="bf16",
                                 specs=["causal;window=1024"] * 5 + ["causal"]),
+    "gemma_local_8k_w1024": dict(B=2, H=16, T=8192, d=128, dtype="bf16", specs=["causal;window=1024"]),
+    "gemma_full_8k_causal": dict(B=2, H=16, T=8192, d=128, dtype="bf16", specs=["causal"]),
     "dilated16k_w512_g2": dict(B=1, H=16, T=16384, d=128, dtype="bf16",
                                specs=["causal;window=512;dilation=2"]),
     "bigbird4k_b8_h12_d64": dict(B=8, H=12, T=4096, d=64, dtype="bf16",
@@ -130,6 +138,89 @@ def load_counter(workload: str, field: str = "hbm_bytes_per_launch"):
 
 def load_traffic(workload: str):
     return load_counter(workload)
+
+
+def _amdsmi_handle(amdsmi):
+    """The amdsmi handle of torch's device 0 (matched by PCI address when
+    several GPUs are listed)."""
+    import torch
+    handles = amdsmi.amdsmi_get_processor_handles()
+    if len(handles) == 1:
+        return handles[0]
+    p = torch.cuda.get_device_properties(0)
+    bdf = "%04x:%02x:%02x.0" % (getattr(p, "pci_domain_id", 0), p.pci_bus_id, p.pci_device_id)
+    for h in handles:
+        if amdsmi.amdsmi_get_gpu_device_bdf(h).lower() == bdf:
+            return h
+    raise RuntimeError(f"no amdsmi device at {bdf}")
+
+
+def sclk_under_load(step, seconds: float):
+    """The GFX clock while the step runs: after the timed region, the step is
+    run back to back for `seconds` while a thread reads amdsmi's current GFX
+    clock every 2 ms.  The reading trails the load by a few hundred ms (it
+    still shows the idle clock at first), so only samples from the last 60%
+    of the window count.  Returns the median and range in MHz, or the error."""
+    import threading
+
+    import torch
+    if seconds <= 0:
+        return None
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = _amdsmi_handle(amdsmi)
+        read = lambda: float(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"])
+        read()
+    except Exception as e:  # no permission, no library: report why
+        return {"mhz": None, "error": f"{type(e).__name__}: {e}"[:200]}
+    samples, stop = [], threading.Event()
+
+    settle = 0.4 * seconds
+
+    def sampler():
+        t_start = time.perf_counter()
+        while not stop.is_set():
+            try:
+                v = read()
+                if time.perf_counter() - t_start >= settle:
+                    samples.append(v)
+            except Exception:
+                pass
+            time.sleep(0.002)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    torch.cuda.synchronize()
+    th.start()
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        step(i)
+        i += 1
+        if i % 4 == 0:
+            torch.cuda.synchronize()  # keep the queue short: samples see the kernels run
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    if not samples:
+        return {"mhz": None, "error": "no samples"}
+    return {"mhz": float(statistics.median(samples)), "min": min(samples), "max": max(samples),
+            "samples": len(samples), "steps": i,
+            "source": f"amdsmi current GFX clock, sampled every 2 ms over the last {seconds - settle:.1f} s "
+                      f"of {seconds:.1f} s of back-to-back steps after the timed region"}
+
+
+def at_clock(roofline: dict, sclk: dict):
+    """Add the fraction of the peak at the recorded clock (the vendor peak is
+    quoted at 2400 MHz) for an MFMA-bound line."""
+    mhz = sclk.get("mhz") if sclk else None
+    if roofline.get("bound") == "mfma" and mhz:
+        peak = roofline["peak"] * mhz / VENDOR_SCLK_MHZ
+        roofline["peak_at_sclk"] = peak
+        roofline["frac_at_sclk"] = roofline["achieved"] / peak
 
 
 def cpu_baseline(wl, specs, q, k, v, budget_s: float):
@@ -254,9 +345,77 @@ def backward_bench(args, wl):
                      "algorithmic_flops_per_step": flops, "algorithmic_bytes_per_step": alg_bytes},
         "cpu_baseline": None,
     }
+    result["sclk"] = sclk_under_load(lambda i: step(), args.sclk_seconds)
+    at_clock(result["roofline"], result["sclk"])
     copy_calibration(args, result)
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = cpu_baseline_backward(spec, q, k, v, g, args.cpu_budget)
+        result["cpu_baseline"]["gpu_over_cpu"] = result["value"] / result["cpu_baseline"]["value"]
     print(json.dumps(result), flush=True)
     return 0
+
+
+def cpu_baseline_backward(spec, q, k, v, g, budget_s: float):
+    """The oracle's backward (dQ, dK, dV in fp64) timed on a bounded sample:
+    the first L positions of up to `threads` heads (the same rule on the
+    shorter sequence; the oracle runs one head per thread), with L grown
+    until one run takes about a second and then scaled to the budget."""
+    import oracle
+    B, H, T, d = q.shape
+    nh = min(B * H, max(1, oracle.threads()))
+    flat = lambda x: x.reshape(B * H, T, d)[:nh].unsqueeze(0)
+    qs, ks, vs, gs = flat(q), flat(k), flat(v), flat(g)
+    L = min(T, 256)
+    while True:
+        t0 = time.perf_counter()
+        oracle.backward(spec, qs[:, :, :L], ks[:, :, :L], vs[:, :, :L], gs[:, :, :L])
+        dt = time.perf_counter() - t0
+        if dt >= 1.0 or L >= T:
+            break
+        L = min(T, L * 2)
+    if L < T and dt < budget_s:
+        # cells grow about linearly in L once L exceeds the band
+        L = min(T, int(L * budget_s / max(dt, 1e-6)))
+        t0 = time.perf_counter()
+        oracle.backward(spec, qs[:, :, :L], ks[:, :, :L], vs[:, :, :L], gs[:, :, :L])
+        dt = time.perf_counter() - t0
+    cells = oracle.count(spec, L) * nh
+    return {"value": cells / dt, "unit": "allowed cells/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"backward of the first {L} positions of {nh} heads of {spec} "
+                      f"({cells} allowed cells), {dt:.1f} s fp64 on the host",
+            "seconds": dt}
+
+
+def cpu_baseline_decode(spec, q, kc, vc, pos, Hkv, budget_s: float):
+    """The oracle timed on decode rows: for each sequence, the new token's row
+    of the forward over the C live cache positions in position order (K and
+    V repeated for the query heads that share a KV head), up to the budget
+    or all B sequences."""
+    import oracle
+    import torch
+    B, H, n_new, d = q.shape
+    C = kc.shape[2]
+    G = H // Hkv
+    t0 = time.perf_counter()
+    cells, done = 0, 0
+    for b in range(B):
+        order = torch.tensor([(pos[b] - C + 1 + x) % C for x in range(C)])
+        kb = kc[b][:, order].repeat_interleave(G, dim=0).unsqueeze(0)
+        vb = vc[b][:, order].repeat_interleave(G, dim=0).unsqueeze(0)
+        qb = torch.zeros(1, H, C, d, dtype=q.dtype)
+        qb[0, :, C - n_new:] = q[b]
+        rows = [(0, h, C - n_new + t) for h in range(H) for t in range(n_new)]
+        _, _, nset = oracle.forward_rows(spec, qb, kb, vb, rows=rows)
+        cells += int(nset.sum())
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": cells / dt, "unit": "allowed cells/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{done} of {B} sequences, all {H} heads x {n_new} new tokens over {C} cached "
+                      f"positions ({cells} allowed cells), {dt:.1f} s fp64 on the host including "
+                      "the per-sequence gather of the ring rows",
+            "seconds": dt}
 
 
 def decode_bench(args, wl):
@@ -330,7 +489,11 @@ def decode_bench(args, wl):
                      "algorithmic_bytes_per_step": alg_bytes},
         "cpu_baseline": None,
     }
+    result["sclk"] = sclk_under_load(lambda i: step(), args.sclk_seconds)
     copy_calibration(args, result)
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = cpu_baseline_decode(spec, q, kc, vc, pos, Hkv, args.cpu_budget)
+        result["cpu_baseline"]["gpu_over_cpu"] = result["value"] / result["cpu_baseline"]["value"]
     print(json.dumps(result), flush=True)
     return 0
 
@@ -344,6 +507,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--sclk-seconds", type=float, default=1.5,
+                    help="after timing, run the step back to back this long while sampling the "
+                         "GFX clock (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a "
                          "known-size kernel for scaling HBM byte counters)")
@@ -462,6 +628,7 @@ def main():
             "mask_specs": specs, "allowed_cells_per_step": E_total,
             "input_copies": n_copies, "parallelism": "single GPU",
         },
+        "us_per_step": ms_per_step * 1e3,
         "effective_tflops": eff_tflops,
         "frac_bf16_peak": eff_tflops / BF16_PEAK_TFLOPS,
         "wall_s_timed": wall,
@@ -469,6 +636,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    result["sclk"] = sclk_under_load(lambda i: step(i), args.sclk_seconds)
+    at_clock(roofline, result["sclk"])
     copy_calibration(args, result)
     if args.cpu_budget > 0:
         q, k, v = host_sets[0]
