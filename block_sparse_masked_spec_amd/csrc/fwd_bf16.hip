@@ -213,16 +213,21 @@ struct WaveState {
 #pragma unroll
             for (int b = 0; b < 2; ++b) s[g][b] = f32x16{};
         // S^T = K Q^T: one K fragment feeds every query group of the wave.
+        // All of the tile's K fragments are read first, then the MFMAs run
+        // (the fragment registers are free again before the V^T reads);
+        // otherwise the scheduler spreads the V^T reads between the QK MFMAs
+        // and every later K fragment waits for all of them.
+        bf16x8 kfa[2 * L::NKS];
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int i = 0; i < 2 * L::NKS; ++i) kfa[i] = *reinterpret_cast<const bf16x8*>(kt + i * 1024 + lane * 16);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ks = 0; ks < L::NKS; ++ks) {
-                const bf16x8 kf =
-                    *reinterpret_cast<const bf16x8*>(kt + (b * L::NKS + ks) * 1024 + lane * 16);
+        for (int i = 0; i < 2 * L::NKS; ++i)
 #pragma unroll
-                for (int g = 0; g < NG; ++g)
-                    s[g][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[g][ks], s[g][b], 0, 0, 0);
-            }
+            for (int g = 0; g < NG; ++g)
+                s[g][i / L::NKS] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfa[i], qf[g][i % L::NKS], s[g][i / L::NKS], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
         // V^T fragment i (two transposed reads).  With one query group the
         // whole tile's fragments are read here, so that they arrive while
         // the softmax runs; with two there is no room and each is read just
