@@ -279,7 +279,10 @@ int oracle_forward_rows(const oracle_mask* m, const float* Q, const float* K,
  *   ds_ij = p_ij (dp_ij - D_i)
  *   dQ_i  = sum_j ds_ij k_j / sqrt(d)
  *   dK_j  = sum_i ds_ij q_i / sqrt(d)
- * Tensors [BH][T][d] fp32 in, fp64 out (dQ, dK, dV written in full).
+ * Written as two passes so that each output is owned by one loop iteration:
+ * a pass over rows i (the weights of S_i, D_i and dQ_i), then a pass over
+ * keys j that visits every row i whose S_i holds j, in increasing i (dK_j,
+ * dV_j).  Tensors [BH][T][d] fp32 in, fp64 out (dQ, dK, dV written in full).
  * Returns 0, or -1 if memory runs out.
  */
 int oracle_backward(const oracle_mask* m, const float* Q, const float* K, const float* V,
@@ -288,63 +291,103 @@ int oracle_backward(const oracle_mask* m, const float* Q, const float* K, const 
     int failed = 0;
     const double rscale = sqrt(1.0 / (double)d);
     for (int64_t x = 0; x < BH * T * d; ++x) dQ[x] = dK[x] = dV[x] = 0.0;
-#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
-    for (int64_t bh = 0; bh < BH; ++bh) {
+    /* per row: the max and the sum of the softmax, and D */
+    double* rmx = (double*)malloc(sizeof(double) * (size_t)(BH * T > 0 ? BH * T : 1));
+    double* rl = (double*)malloc(sizeof(double) * (size_t)(BH * T > 0 ? BH * T : 1));
+    double* rD = (double*)malloc(sizeof(double) * (size_t)(BH * T > 0 ? BH * T : 1));
+    if (!rmx || !rl || !rD) {
+        free(rmx);
+        free(rl);
+        free(rD);
+        return -1;
+    }
+    /* pass 1: rows */
+#pragma omp parallel reduction(| : failed)
+    {
         int64_t* set = (int64_t*)malloc(sizeof(int64_t) * (size_t)(T > 0 ? T : 1));
         double* p = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
         double* dp = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
-        if (!set || !p || !dp) {
-            failed = 1;
-        } else {
-            for (int64_t i = 0; i < T; ++i) {
-                const float* q = Q + (bh * T + i) * d;
-                const float* g = dO + (bh * T + i) * d;
-                const int64_t n = oracle_row_set(m, T, i, set);
-                if (n == 0) continue;
-                /* softmax weights over S_i */
-                double mx = -INFINITY;
-                for (int64_t t = 0; t < n; ++t) {
-                    const float* kr = K + d * (bh * T + set[t]);
-                    double qk = 0.0;
-                    for (int64_t c = 0; c < d; ++c) qk += (double)q[c] * (double)kr[c];
-                    p[t] = qk * rscale;
-                    if (p[t] > mx) mx = p[t];
-                }
-                double l = 0.0;
-                for (int64_t t = 0; t < n; ++t) {
-                    p[t] = exp(p[t] - mx);
-                    l += p[t];
-                }
-                for (int64_t t = 0; t < n; ++t) p[t] /= l;
-                /* dp and D */
-                double D = 0.0;
-                for (int64_t t = 0; t < n; ++t) {
-                    const float* vr = V + d * (bh * T + set[t]);
-                    double gv = 0.0;
-                    for (int64_t c = 0; c < d; ++c) gv += (double)g[c] * (double)vr[c];
-                    dp[t] = gv;
-                    D += p[t] * gv;
-                }
-                /* accumulate the three gradients */
-                double* dq = dQ + (bh * T + i) * d;
-                for (int64_t t = 0; t < n; ++t) {
-                    const int64_t j = set[t];
-                    const double ds = p[t] * (dp[t] - D);
-                    const float* kr = K + d * (bh * T + j);
-                    double* dk = dK + d * (bh * T + j);
-                    double* dv = dV + d * (bh * T + j);
-                    for (int64_t c = 0; c < d; ++c) {
-                        dq[c] += ds * (double)kr[c] * rscale;
-                        dk[c] += ds * (double)q[c] * rscale;
-                        dv[c] += p[t] * (double)g[c];
-                    }
-                }
+        if (!set || !p || !dp) failed = 1;
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < BH * T; ++r) {
+            if (failed) continue;
+            const int64_t bh = r / T, i = r % T;
+            const float* q = Q + (bh * T + i) * d;
+            const float* g = dO + (bh * T + i) * d;
+            const int64_t n = oracle_row_set(m, T, i, set);
+            rmx[r] = 0.0;
+            rl[r] = 0.0;
+            rD[r] = 0.0;
+            if (n == 0) continue;
+            /* softmax weights over S_i */
+            double mx = -INFINITY;
+            for (int64_t t = 0; t < n; ++t) {
+                const float* kr = K + d * (bh * T + set[t]);
+                double qk = 0.0;
+                for (int64_t c = 0; c < d; ++c) qk += (double)q[c] * (double)kr[c];
+                p[t] = qk * rscale;
+                if (p[t] > mx) mx = p[t];
+            }
+            double l = 0.0;
+            for (int64_t t = 0; t < n; ++t) {
+                p[t] = exp(p[t] - mx);
+                l += p[t];
+            }
+            for (int64_t t = 0; t < n; ++t) p[t] /= l;
+            /* dp and D */
+            double D = 0.0;
+            for (int64_t t = 0; t < n; ++t) {
+                const float* vr = V + d * (bh * T + set[t]);
+                double gv = 0.0;
+                for (int64_t c = 0; c < d; ++c) gv += (double)g[c] * (double)vr[c];
+                dp[t] = gv;
+                D += p[t] * gv;
+            }
+            rmx[r] = mx;
+            rl[r] = l;
+            rD[r] = D;
+            /* dQ_i */
+            double* dq = dQ + (bh * T + i) * d;
+            for (int64_t t = 0; t < n; ++t) {
+                const double ds = p[t] * (dp[t] - D);
+                const float* kr = K + d * (bh * T + set[t]);
+                for (int64_t c = 0; c < d; ++c) dq[c] += ds * (double)kr[c] * rscale;
             }
         }
         free(set);
         free(p);
         free(dp);
     }
+    /* pass 2: keys, each over the rows that read it */
+    if (!failed) {
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int64_t col = 0; col < BH * T; ++col) {
+            const int64_t bh = col / T, j = col % T;
+            const float* kr = K + d * (bh * T + j);
+            const float* vr = V + d * (bh * T + j);
+            double* dk = dK + d * (bh * T + j);
+            double* dv = dV + d * (bh * T + j);
+            for (int64_t i = 0; i < T; ++i) {
+                if (!oracle_allowed_T(m, T, i, j)) continue;
+                const int64_t r = bh * T + i;
+                const float* q = Q + d * r;
+                const float* g = dO + d * r;
+                double qk = 0.0;
+                for (int64_t c = 0; c < d; ++c) qk += (double)q[c] * (double)kr[c];
+                const double pij = exp(qk * rscale - rmx[r]) / rl[r];
+                double gv = 0.0;
+                for (int64_t c = 0; c < d; ++c) gv += (double)g[c] * (double)vr[c];
+                const double ds = pij * (gv - rD[r]);
+                for (int64_t c = 0; c < d; ++c) {
+                    dk[c] += ds * (double)q[c] * rscale;
+                    dv[c] += pij * (double)g[c];
+                }
+            }
+        }
+    }
+    free(rmx);
+    free(rl);
+    free(rD);
     return failed ? -1 : 0;
 }
 

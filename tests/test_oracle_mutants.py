@@ -57,7 +57,10 @@ MUTANTS = [
     ("bwd_delta_dropped", "const double ds = p[t] * (dp[t] - D);", "const double ds = p[t] * dp[t];"),
     ("bwd_dk_uses_k", "dk[c] += ds * (double)q[c] * rscale;", "dk[c] += ds * (double)kr[c] * rscale;"),
     ("bwd_dq_unscaled", "dq[c] += ds * (double)kr[c] * rscale;", "dq[c] += ds * (double)kr[c];"),
-    ("bwd_dv_unnormalised", "for (int64_t t = 0; t < n; ++t) p[t] /= l;", ""),
+    ("bwd_row_weights_unnormalised", "for (int64_t t = 0; t < n; ++t) p[t] /= l;", ""),
+    ("bwd_key_weights_unnormalised", "exp(qk * rscale - rmx[r]) / rl[r];", "exp(qk * rscale - rmx[r]);"),
+    ("bwd_key_delta_dropped", "const double ds = pij * (gv - rD[r]);", "const double ds = pij * gv;"),
+    ("bwd_dv_uses_q", "dv[c] += pij * (double)g[c];", "dv[c] += pij * (double)q[c];"),
     ("bwd_dp_uses_k", "const float* vr = V + d * (bh * T + set[t]);", "const float* vr = K + d * (bh * T + set[t]);"),
     ("block_globals_dropped", "return local || rnd || strided_col(m, j) || global_pair(m, i, j);",
      "return local || rnd || strided_col(m, j);"),
