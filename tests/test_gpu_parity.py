@@ -2,8 +2,9 @@
 
 Tolerances (fixed in the test, read from the stated targets):
 * bf16 inputs: elementwise |O_gpu - O_oracle| <= 2e-2;
-* fp32 inputs: per-row normwise max|o - o*| / max|o*| <= 1e-5 (elementwise
-  relative error is ill-posed where |o*| is near 0; it is reported too).
+* fp32 inputs: per-row normwise max|o - o*| / max|o*| <= 1e-5, and
+  elementwise |o - o*| / |o*| <= 1e-5 wherever |o*| >= 0.05 (elementwise
+  relative error is ill-posed where |o*| is near 0; there it is reported).
 Integer outputs (counts, tile maps) are checked bit-exact in the CPU suite.
 """
 import sys
@@ -21,6 +22,7 @@ pytestmark = pytest.mark.gpu
 
 BF16_ATOL = 2e-2
 F32_ROWREL = 1e-5
+F32_ELEM_FLOOR = 0.05  # elementwise relative error asserted where |o*| >= this
 
 
 def announce(msg):
@@ -50,16 +52,29 @@ def check_bf16(got, ref, what=""):
     return err
 
 
-def check_f32(got, ref, what=""):
+def check_f32(got, ref, what="", elementwise=False):
+    """Per-row normwise relative error <= 1e-5; with `elementwise` also the
+    elementwise relative error <= 1e-5 over every entry with |o*| >=
+    F32_ELEM_FLOOR.  Entries nearer 0 are the cancellation cases where an
+    exact fp32 kernel already misses a relative bound (absolute error ~1e-7
+    against |o*| ~ 0); their largest relative error is reported only."""
     g = got.double().numpy().reshape(-1, ref.shape[-1])
     r = ref.reshape(-1, ref.shape[-1])
     assert np.isfinite(g).all(), f"non-finite output {what}"
     rowrel = (np.abs(g - r).max(-1) / np.abs(r).max(-1)).max()
     assert rowrel <= F32_ROWREL, f"row-normwise rel err {rowrel:.3e} > {F32_ROWREL} {what}"
+    rel = np.abs(g - r) / np.maximum(np.abs(r), 1e-300)
+    big = np.abs(r) >= F32_ELEM_FLOOR
+    elem = float(rel[big].max()) if big.any() else 0.0
+    small = float(rel[~big].max()) if (~big).any() else 0.0
+    announce(f"fp32 {what}: row-normwise {rowrel:.2e}, elementwise (|o*| >= {F32_ELEM_FLOOR}) "
+             f"{elem:.2e}, elementwise below the floor {small:.2e}")
+    if elementwise:
+        assert elem <= F32_ROWREL, f"elementwise rel err {elem:.3e} > {F32_ROWREL} (|o*| >= {F32_ELEM_FLOOR}) {what}"
     return rowrel
 
 
-def full_check(sa, spec, B, H, T, d, dtype, seed, scale_q=1.0):
+def full_check(sa, spec, B, H, T, d, dtype, seed, scale_q=1.0, elementwise=False):
     q, k, v = inputs.qkv(B, H, T, d, dtype, seed)
     if scale_q != 1.0:
         q = inputs.scaled(q, scale_q)
@@ -67,16 +82,18 @@ def full_check(sa, spec, B, H, T, d, dtype, seed, scale_q=1.0):
     ref, _, _ = oracle.forward_rows(spec, q, k, v)
     if dtype == "bf16":
         return check_bf16(got, ref, f"{spec} T={T} d={d}")
-    return check_f32(got, ref, f"{spec} T={T} d={d}")
+    return check_f32(got, ref, f"{spec} T={T} d={d}", elementwise)
 
 
 # --------------------------------------------------------- tiny oracle config
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_tiny_fp32_window2_stride4(gpu, seed):
-    """B=1, H=1, T=16, d=16, fp32; causal window 2 + columns j%4==3 (52 cells)."""
+    """B=1, H=1, T=16, d=16, fp32; causal window 2 + columns j%4==3 (52 cells).
+    Both the per-row normwise and the elementwise relative error (entries
+    with |o*| >= 0.05) must be within 1e-5."""
     spec = "causal;window=2;stride=4;phase=3"
     assert gpu.sparse_attn_count(spec, 16) == 52
-    full_check(gpu, spec, 1, 1, 16, 16, "f32", seed)
+    full_check(gpu, spec, 1, 1, 16, 16, "f32", seed, elementwise=True)
 
 
 # ------------------------------------------------ small shapes, ragged tails
