@@ -143,8 +143,8 @@ class PlanCache {
         dp.n_parts = hp.n_parts;
         dp.n_split = static_cast<int32_t>(hp.split_qb.size());
         size_t off = 0;
-        auto section = [&](size_t bytes, size_t* where) {
-            off = align_up(off, 16);
+        auto section = [&](size_t bytes, size_t* where, size_t align = 16) {
+            off = align_up(off, align);
             *where = off;
             off += bytes;
         };
@@ -161,6 +161,7 @@ class PlanCache {
         section(hp.item_part.size() * 4, &dp.off_item_part);
         section(hp.split_qb.size() * 4, &dp.off_split_qb);
         section(hp.split_ptr.size() * 4, &dp.off_split_ptr);
+        section(hp.item_rec.size() * 4, &dp.off_item_rec, sizeof(int32_t) * sa::kItemRec);
         dp.bytes = align_up(off, 16) + 16;
         std::vector<unsigned char> host(dp.bytes, 0);
         auto put = [&](size_t where, const void* src, size_t bytes) {
@@ -179,6 +180,7 @@ class PlanCache {
         put(dp.off_item_part, hp.item_part.data(), hp.item_part.size() * 4);
         put(dp.off_split_qb, hp.split_qb.data(), hp.split_qb.size() * 4);
         put(dp.off_split_ptr, hp.split_ptr.data(), hp.split_ptr.size() * 4);
+        put(dp.off_item_rec, hp.item_rec.data(), hp.item_rec.size() * 4);
         Upload up;
         int rc = upload(host, stream, dev, &up);
         if (rc != SA_OK) return rc;
@@ -431,6 +433,7 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     a.bq = bq;
     a.item_qb = reinterpret_cast<const int32_t*>(base + dp.off_item_qb);
     a.item_part = dp.n_parts > 0 ? reinterpret_cast<const int32_t*>(base + dp.off_item_part) : nullptr;
+    a.item_rec = reinterpret_cast<const int32_t*>(base + dp.off_item_rec);
     a.part = nullptr;
     a.n_parts = dp.n_parts;
     std::unique_lock<std::mutex> ws_hold;
@@ -546,6 +549,7 @@ int backward(int dtype, const void* Q, const void* K, const void* V, const void*
     a.bq = bq;
     a.item_qb = reinterpret_cast<const int32_t*>(base + dp.off_item_qb);
     a.item_part = dp.n_parts > 0 ? reinterpret_cast<const int32_t*>(base + dp.off_item_part) : nullptr;
+    a.item_rec = reinterpret_cast<const int32_t*>(base + dp.off_item_rec);
     a.part = nullptr;
     a.n_parts = dp.n_parts;
     b.dO = dO;

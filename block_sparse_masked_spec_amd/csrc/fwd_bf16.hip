@@ -46,6 +46,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+static_assert(sizeof(i32x16) == sizeof(int32_t) * kItemRec, "one item record");
 
 typedef const __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
@@ -137,50 +139,86 @@ __device__ __forceinline__ void v_piece(int gi, int lane, int* row, int* col) {
     *col = db * 32 + (g & 1) * 16 + (L & 3) * 4;
 }
 
-// Issue the direct loads of one K tile and one V tile (this wave's share).
-// Slots that hold no key (past T, or unused gather slots) copy a valid row;
-// the mask gives them zero weight.  Gather keys are read before the first
-// load is issued, so no wait lands between the loads.
+// The direct loads of one K tile and one V tile (this wave's share), as
+// buffer loads into LDS.  A lane's piece of an in-place tile sits at a fixed
+// byte offset from the tile's first row (computed once), and the tile's
+// first row is a scalar offset: issuing a tile costs no vector arithmetic.
+// Only a tile that runs past T takes per-lane offsets, with its missing rows
+// clamped to row T - 1 (the mask gives them zero weight), and so do
+// gathered tiles, whose keys are read from the plan before the first load is
+// issued (no wait lands between the loads).  Each kind of tile issues its
+// own loads: were the paths joined before the loads, the in-place path would
+// inherit the wait on the gathered path's key reads -- and, since vector
+// loads complete in order, on every load in flight.  The marker after each
+// path's loads keeps the compiler from merging them.
 template <int D, int NW>
 struct TileLoad {
-static __device__ __forceinline__ void issue(const Cursor& c, const FwdArgs& a, const __bf16* Kp,
-                                             const __bf16* Vp, char* kdst, char* vdst, int wave,
-                                             int lane, int T, int ga0, int gna, int gb0, size_t rs) {
     using L = Lay<D, NW>;
-    int kkey[L::LOADS_PER_WAVE], vkey[L::LOADS_PER_WAVE];
-    int kcol[L::LOADS_PER_WAVE], vcol[L::LOADS_PER_WAVE];
-    if (c.inplace()) {
-        const int k0 = c.kb * kBK;
+    __amdgpu_buffer_rsrc_t krsrc, vrsrc;
+    int rowb;                                  // bytes between key rows
+    int wave;
+    int kr[L::LOADS_PER_WAVE], vr[L::LOADS_PER_WAVE];      // tile row of each piece
+    int koff[L::LOADS_PER_WAVE], voff[L::LOADS_PER_WAVE];  // byte offset in the tile
+
+    __device__ __forceinline__ TileLoad(const __bf16* Kp, const __bf16* Vp, int T, size_t rs, int wave_,
+                                        int lane)
+        : rowb(int(rs) * 2), wave(wave_) {
+        // The sequence's rows span at most T * rs elements (at most 1 GiB for
+        // T <= SA_MAX_T), so every offset fits the buffer's 32 bits.
+        const int bytes = int(size_t(T) * rs * 2);
+        krsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Kp), 0, bytes, 0x00020000);
+        vrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Vp), 0, bytes, 0x00020000);
 #pragma unroll
         for (int i = 0; i < L::LOADS_PER_WAVE; ++i) {
             const int gi = wave * L::LOADS_PER_WAVE + i;
-            int kr, vr;
-            k_piece<D>(gi, lane, &kr, &kcol[i]);
-            v_piece<D>(gi, lane, &vr, &vcol[i]);
-            kkey[i] = min(k0 + kr, T - 1);
-            vkey[i] = min(k0 + vr, T - 1);
+            int kc, vc;
+            k_piece<D>(gi, lane, &kr[i], &kc);
+            v_piece<D>(gi, lane, &vr[i], &vc);
+            koff[i] = kr[i] * rowb + kc * 2;
+            voff[i] = vr[i] * rowb + vc * 2;
         }
-    } else {
+    }
+
+    __device__ __forceinline__ void put(char* kdst, char* vdst, const int (&ko)[L::LOADS_PER_WAVE],
+                                        const int (&vo)[L::LOADS_PER_WAVE], int soff) const {
 #pragma unroll
         for (int i = 0; i < L::LOADS_PER_WAVE; ++i) {
             const int gi = wave * L::LOADS_PER_WAVE + i;
-            int kr, vr;
-            k_piece<D>(gi, lane, &kr, &kcol[i]);
-            v_piece<D>(gi, lane, &vr, &vcol[i]);
-            const int ks = min(c.gi + kr, c.g_total - 1), vs = min(c.gi + vr, c.g_total - 1);
-            kkey[i] = a.colkeys[ks < gna ? ga0 + ks : gb0 + (ks - gna)];
-            vkey[i] = a.colkeys[vs < gna ? ga0 + vs : gb0 + (vs - gna)];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, as_lds(kdst + gi * 1024), 16, ko[i], soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, as_lds(vdst + gi * 1024), 16, vo[i], soff, 0, 0);
         }
     }
+
+    __device__ __forceinline__ void issue(const Cursor& c, const FwdArgs& a, char* kdst, char* vdst, int T,
+                                          int ga0, int gna, int gb0) const {
+        int ko[L::LOADS_PER_WAVE], vo[L::LOADS_PER_WAVE];
+        if (c.inplace()) {
+            const int k0 = c.kb * kBK;
+            if (k0 + kBK <= T) {
+                put(kdst, vdst, koff, voff, k0 * rowb);
+                asm volatile("; tile loads issued: in place" ::: "memory");
+            } else {
 #pragma unroll
-    for (int i = 0; i < L::LOADS_PER_WAVE; ++i) {
-        const int gi = wave * L::LOADS_PER_WAVE + i;
-        __builtin_amdgcn_global_load_lds(as_global(Kp + size_t(kkey[i]) * rs + kcol[i]),
-                                         as_lds(kdst + gi * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(as_global(Vp + size_t(vkey[i]) * rs + vcol[i]),
-                                         as_lds(vdst + gi * 1024), 16, 0, 0);
+                for (int i = 0; i < L::LOADS_PER_WAVE; ++i) {
+                    ko[i] = koff[i] + (min(k0 + kr[i], T - 1) - kr[i]) * rowb;
+                    vo[i] = voff[i] + (min(k0 + vr[i], T - 1) - vr[i]) * rowb;
+                }
+                put(kdst, vdst, ko, vo, 0);
+                asm volatile("; tile loads issued: past T" ::: "memory");
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < L::LOADS_PER_WAVE; ++i) {
+                const int ks = min(c.gi + kr[i], c.g_total - 1), vs = min(c.gi + vr[i], c.g_total - 1);
+                const int kkey = a.colkeys[ks < gna ? ga0 + ks : gb0 + (ks - gna)];
+                const int vkey = a.colkeys[vs < gna ? ga0 + vs : gb0 + (vs - gna)];
+                ko[i] = koff[i] + (kkey - kr[i]) * rowb;
+                vo[i] = voff[i] + (vkey - vr[i]) * rowb;
+            }
+            put(kdst, vdst, ko, vo, 0);
+            asm volatile("; tile loads issued: gathered keys" ::: "memory");
+        }
     }
-}
 };
 
 // End of a tile: this wave's direct loads of the next tile have landed and
@@ -326,21 +364,18 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
     constexpr int BQ = NW * NG * 32;  // waves x groups x 32 queries = one query block
     static_assert(BQ == kBQ || BQ == 64, "query blocks of the plans: 128 or 64 rows");
     using L = Lay<D, NW>;
-    // Two buffers as distinct objects, indexed statically (the loop below is
-    // unrolled by two), so the compiler can tell the prefetch into one from
-    // the reads of the other and keeps the prefetch in flight.
-    __shared__ __attribute__((aligned(1024))) char kbuf0[L::TILE];
-    __shared__ __attribute__((aligned(1024))) char vbuf0[L::TILE];
-    __shared__ __attribute__((aligned(1024))) char kbuf1[L::TILE];
-    __shared__ __attribute__((aligned(1024))) char vbuf1[L::TILE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // The wave index is uniform across the wave; readfirstlane lets the
+    // compiler keep it, and every address derived from it, in scalar registers.
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, h = lane >> 5;
     const int work = xcd_slice_index(blockIdx.x, gridDim.x);
     const int n_items = gridDim.x / a.BH;
     const int bh = work / n_items;
-    const int it = ldc(a.qb_order, work % n_items);  // work item: a query block or part of one
-    const int qb = ldc(a.item_qb, it);
+    // The work item (a query block or part of one): its whole record in one
+    // scalar load, so the first tile's loads wait on a single read.
+    const i32x16 rec = ldc(reinterpret_cast<const i32x16*>(a.item_rec), work % n_items);
+    const int qb = rec[REC_QB];
     const int T = a.T;
     // Row stride and base of this sequence; with SUB, sequence bh is residue
     // class bh % sub of the full sequence bh / sub.
@@ -352,6 +387,7 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
     const __bf16* Vp = static_cast<const __bf16*>(a.V) + base;
     __bf16* Op = static_cast<__bf16*>(a.O) + base;
     const int q_base = qb * BQ + wave * NG * 32;
+    const TileLoad<D, NW> ld(Kp, Vp, T, rs, wave, lane);
 
     WaveState<D, NG, NW> st;
     bool rowg[NG];
@@ -370,16 +406,17 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
         for (int db = 0; db < L::NDB; ++db) st.acc[g][db] = f32x16{};
         st.m_run[g] = -1e30f;
         st.l_run[g] = 0.f;
-        rowg[g] = qi < T && ((a.rowbits[qi >> 5] >> (qi & 31)) & 1u);
+        // A group's 32 queries share one word of the global-row bits (read
+        // through the scalar cache, so it adds no wait on the Q loads).
+        const uint32_t rw = ldc(a.rowbits, min(q_base + g * 32, T - 1) >> 5);
+        rowg[g] = qi < T && ((rw >> n) & 1u);
         qres[g] = a.dil == 1 ? 0 : qi % a.dil;
         qblk[g] = a.blk > 0 ? min(qi, T - 1) / a.blk : 0;
     }
 
-    const int ga0 = ldc(a.gseg, 4 * it), ga1 = ldc(a.gseg, 4 * it + 1);
-    const int gb0 = ldc(a.gseg, 4 * it + 2), gb1 = ldc(a.gseg, 4 * it + 3);
-    const int gna = ga1 - ga0;
-    Cursor cur{ldc(a.run_ptr, it), ldc(a.run_ptr, it + 1), 0, 0, false, 0, gna + (gb1 - gb0)};
-    cursor_enter_run(cur, a);
+    const int ga0 = rec[REC_GA0], gna = rec[REC_GA1] - ga0, gb0 = rec[REC_GB0];
+    Cursor cur{rec[REC_RUN_BEGIN], rec[REC_RUN_END], rec[REC_FIRST_KB], rec[REC_FIRST_END] & 0x7fffffff,
+               rec[REC_FIRST_END] < 0, 0, gna + (rec[REC_GB1] - gb0)};
 
     auto run_tile = [&](const Cursor& c, const char* kt, const char* vt) {
         const bool masked = !c.inplace() || c.masked;
@@ -396,19 +433,26 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
         st.tile(kt, vt, a, lane, masked, allowed);
     };
 
-    if (!cur.done()) TileLoad<D, NW>::issue(cur, a, Kp, Vp, kbuf0, vbuf0, wave, lane, T, ga0, gna, gb0, rs);
+    // Two buffers as distinct objects, indexed statically (the loop below is
+    // unrolled by two), so the compiler can tell the prefetch into one from
+    // the reads of the other and keeps the prefetch in flight.
+    __shared__ __attribute__((aligned(1024))) char kbuf0[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char vbuf0[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char kbuf1[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char vbuf1[L::TILE];
+    if (!cur.done()) ld.issue(cur, a, kbuf0, vbuf0, T, ga0, gna, gb0);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed
     __syncthreads();                // ... and the other waves'
     while (!cur.done()) {
         Cursor nxt = cur;
         cursor_advance(nxt, a);
-        if (!nxt.done()) TileLoad<D, NW>::issue(nxt, a, Kp, Vp, kbuf1, vbuf1, wave, lane, T, ga0, gna, gb0, rs);
+        if (!nxt.done()) ld.issue(nxt, a, kbuf1, vbuf1, T, ga0, gna, gb0);
         run_tile(cur, kbuf0, vbuf0);
         tile_barrier();
         if (nxt.done()) break;
         cur = nxt;
         cursor_advance(nxt, a);
-        if (!nxt.done()) TileLoad<D, NW>::issue(nxt, a, Kp, Vp, kbuf0, vbuf0, wave, lane, T, ga0, gna, gb0, rs);
+        if (!nxt.done()) ld.issue(nxt, a, kbuf0, vbuf0, T, ga0, gna, gb0);
         run_tile(cur, kbuf1, vbuf1);
         tile_barrier();
         cur = nxt;
@@ -416,7 +460,7 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
 
     // Epilogue: O = acc / l (both lane halves' sums), or -- for one part of
     // a split block -- acc, the running max and l into the item's slot.
-    const int part = a.item_part ? ldc(a.item_part, it) : -1;
+    const int part = rec[REC_PART];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const int qi = q_base + g * 32 + n;

@@ -120,8 +120,30 @@ struct HostPlan {
     std::vector<uint32_t> rowbits;  // bit i%32 of word i/32: row i is global
     std::vector<int32_t> blk_ptr;   // block mode: copies of MaskRule::iv_ptr/ivals
     std::vector<int32_t> blk_iv;
+    // The fast kernel's view of the items: kItemRec ints per item, in
+    // qb_order's order, so that one scalar load gives a workgroup all of it
+    // (see ItemRec for the fields).
+    std::vector<int32_t> item_rec;
     int64_t inplace_tiles = 0, masked_tiles = 0, gathered_tiles = 0, gathered_keys = 0;
 };
+
+// Fields of one item record.  FIRST_KB / FIRST_END repeat the item's first
+// run (FIRST_END carries the run's mask flag in bit 31), so the first tile
+// can be addressed without a dependent read; both are 0 when the item has
+// no in-place run.
+enum ItemRec : int {
+    REC_QB = 0,
+    REC_PART,
+    REC_RUN_BEGIN,
+    REC_RUN_END,
+    REC_GA0,
+    REC_GA1,
+    REC_GB0,
+    REC_GB1,
+    REC_FIRST_KB,
+    REC_FIRST_END,
+};
+constexpr int kItemRec = 16;
 
 // split_cap: 0 = one item per query block; kSplitAuto = split blocks above
 // max(kSplitMinTiles, twice the mean tile count); n > 0 = split blocks above
@@ -137,7 +159,7 @@ struct DevicePlan {
     int32_t n_qb = 0, n_items = 0, n_parts = 0, n_split = 0;
     size_t off_qb_order = 0, off_run_ptr = 0, off_runs = 0, off_gseg = 0, off_colkeys = 0,
            off_colbits = 0, off_rowbits = 0, off_blk_ptr = 0, off_blk_iv = 0, off_item_qb = 0,
-           off_item_part = 0, off_split_qb = 0, off_split_ptr = 0;
+           off_item_part = 0, off_split_qb = 0, off_split_ptr = 0, off_item_rec = 0;
 };
 
 // Device-resident backward plan (one allocation).
@@ -186,6 +208,7 @@ struct FwdArgs {
     // [BH][n_parts][bq] float2 (running max in log2 units, row sum).
     const int32_t* item_qb;    // null: item = query block
     const int32_t* item_part;  // null: no partial slots
+    const int32_t* item_rec;   // kItemRec ints per item, in qb_order's order
     float* part;
     int32_t n_parts;
 };

@@ -302,6 +302,20 @@ HostPlan build_plan(const MaskRule& rule, int32_t bq, int32_t bk, int64_t split_
     std::iota(p.qb_order.begin(), p.qb_order.end(), 0);
     std::stable_sort(p.qb_order.begin(), p.qb_order.end(),
                      [&](int32_t x, int32_t y) { return item_work[x] > item_work[y]; });
+    p.item_rec.assign(size_t(p.n_items) * kItemRec, 0);
+    for (int32_t w = 0; w < p.n_items; ++w) {
+        const int32_t it = p.qb_order[w];
+        int32_t* r = p.item_rec.data() + size_t(w) * kItemRec;
+        r[REC_QB] = p.item_qb[it];
+        r[REC_PART] = p.item_part[it];
+        r[REC_RUN_BEGIN] = p.run_ptr[it];
+        r[REC_RUN_END] = p.run_ptr[it + 1];
+        for (int x = 0; x < 4; ++x) r[REC_GA0 + x] = p.gseg[4 * size_t(it) + x];
+        if (r[REC_RUN_BEGIN] < r[REC_RUN_END]) {
+            r[REC_FIRST_KB] = p.runs[2 * size_t(r[REC_RUN_BEGIN])];
+            r[REC_FIRST_END] = p.runs[2 * size_t(r[REC_RUN_BEGIN]) + 1];
+        }
+    }
     return p;
 }
 

@@ -138,6 +138,18 @@ int check(const std::string& spec, int T, int bq, int64_t cap) {
         if (o < 0 || o >= sp.n_items || seen[o]) return fail("order is not a permutation", spec, T, bq, cap);
         seen[o] = 1;
         if (x > 0 && work[sp.qb_order[x - 1]] < work[o]) return fail("order not heaviest first", spec, T, bq, cap);
+        // The fast kernel reads item x of the launch from its record alone.
+        if (sp.item_rec.size() != size_t(sp.n_items) * sa::kItemRec) return fail("record count", spec, T, bq, cap);
+        const int32_t* r = sp.item_rec.data() + size_t(x) * sa::kItemRec;
+        bool ok = r[sa::REC_QB] == sp.item_qb[o] && r[sa::REC_PART] == sp.item_part[o] &&
+                  r[sa::REC_RUN_BEGIN] == sp.run_ptr[o] && r[sa::REC_RUN_END] == sp.run_ptr[o + 1];
+        for (int g = 0; g < 4; ++g) ok = ok && r[sa::REC_GA0 + g] == sp.gseg[4 * size_t(o) + g];
+        if (sp.run_ptr[o] < sp.run_ptr[o + 1])
+            ok = ok && r[sa::REC_FIRST_KB] == sp.runs[2 * size_t(sp.run_ptr[o])] &&
+                 r[sa::REC_FIRST_END] == sp.runs[2 * size_t(sp.run_ptr[o]) + 1];
+        else
+            ok = ok && r[sa::REC_FIRST_KB] == 0 && r[sa::REC_FIRST_END] == 0;
+        if (!ok) return fail("item record differs from the plan arrays", spec, T, bq, cap);
     }
     return 0;
 }
