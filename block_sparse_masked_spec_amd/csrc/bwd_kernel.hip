@@ -425,6 +425,74 @@ __device__ __forceinline__ void dma_rows2(__bf16* dst_a, __bf16* dst_b, const __
     }
 }
 
+// The same tile fill with buffer loads into LDS, for tiles of 64 keys.  The
+// rows of one wave's pieces are NW * RPI apart -- a multiple of 16, so every
+// piece of a lane has the same swizzled chunk -- and a piece's byte offset
+// from the tile's first row is the first piece's plus a scalar step.  Issuing
+// a tile of consecutive rows then takes a lane's first row r0 and that offset
+// (a few instructions from the lane id, recomputed at each issue so that
+// they hold no register across the loop), with the tile's first row and the
+// step as scalar offsets.  A tile past T clamps its rows to T - 1 per lane,
+// and a tile of listed rows takes per-lane offsets.
+template <int D, int NW>
+struct DmaTile {
+    static constexpr int CPR = D / 8;     // 16-byte chunks per row
+    static constexpr int RPI = 64 / CPR;  // rows per instruction
+    static constexpr int NJ = CPR / NW;   // instructions per wave and tensor
+    static constexpr int ROWB = D * 2;    // bytes per row
+    static constexpr int STEP = NW * RPI;
+    static_assert(STEP % 16 == 0, "pieces of one lane share their swizzle");
+    int wave, lane;
+
+    __device__ __forceinline__ DmaTile(int wave_, int lane_) : wave(wave_), lane(lane_) {}
+    __device__ __forceinline__ int first_row() const { return wave * RPI + lane / CPR; }
+    __device__ __forceinline__ int first_off(int r0) const {
+        return r0 * ROWB + ((lane % CPR) ^ swz<D>(r0)) * 16;
+    }
+    template <typename VOff, typename SOff>
+    __device__ __forceinline__ void put(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, __bf16* da,
+                                        __bf16* db, VOff vo, SOff so) const {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int lds = (wave + j * NW) * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, as_lds(reinterpret_cast<char*>(da) + lds), 16, vo(j),
+                                                     so(j), 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, as_lds(reinterpret_cast<char*>(db) + lds), 16, vo(j),
+                                                     so(j), 0, 0);
+        }
+    }
+    // Rows k0 .. k0 + 63, those past T clamped to row T - 1.
+    __device__ __forceinline__ void rows_from(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, __bf16* da,
+                                              __bf16* db, int k0, int T) const {
+        const int r0 = first_row(), off0 = first_off(r0);
+        if (k0 + 64 <= T) {
+            put(ra, rb, da, db, [&](int) { return off0; }, [&](int j) { return (k0 + j * STEP) * ROWB; });
+            asm volatile("; tile loads issued: in place" ::: "memory");
+        } else {
+            put(ra, rb, da, db,
+                [&](int j) { return off0 + (min(k0 + r0 + j * STEP, T - 1) - r0) * ROWB; },
+                [&](int) { return 0; });
+            asm volatile("; tile loads issued: past T" ::: "memory");
+        }
+    }
+    // Tile row r comes from source row row_of(r) (a valid row).
+    template <typename RowOf>
+    __device__ __forceinline__ void rows_listed(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                                __bf16* da, __bf16* db, RowOf row_of) const {
+        const int r0 = first_row(), off0 = first_off(r0);
+        int vo[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) vo[j] = off0 + (row_of(r0 + j * STEP) - r0) * ROWB;
+        put(ra, rb, da, db, [&](int j) { return vo[j]; }, [&](int) { return 0; });
+        asm volatile("; tile loads issued: listed rows" ::: "memory");
+    }
+};
+
+// Buffer resource over the n bytes at p (raw addressing, no stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p, int n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
+}
+
 // Product of rows blk*32 .. blk*32+31 of a swizzled 64-row tile with this
 // lane's fragments: out = rows . frag^T (rows are MFMA rows in the permuted
 // order, one column per lane).
@@ -543,8 +611,6 @@ __global__ __launch_bounds__(NW * 64, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
     using F = typename Ops<E>::frag;
     const FwdArgs& a = b.f;
     constexpr int TILE = kBK * D;
-    __shared__ __attribute__((aligned(1024))) E kbuf[2 * TILE];
-    __shared__ __attribute__((aligned(1024))) E vbuf[2 * TILE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -552,8 +618,9 @@ __global__ __launch_bounds__(NW * 64, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
     const int work = xcd_slice_index(blockIdx.x, gridDim.x);
     const int n_items = gridDim.x / a.BH;
     const int bh = work / n_items;
-    const int it = ldc(a.qb_order, work % n_items);  // a query block or one key range of it
-    const int qb = ldc(a.item_qb, it);
+    // The work item (a query block or one key range of it) from its record.
+    const int32_t* rec = a.item_rec + size_t(work % n_items) * kItemRec;
+    const int qb = ldc(rec, REC_QB);
     const int T = a.T;
     const size_t base = size_t(bh) * size_t(T) * D;
     const E* Qp = static_cast<const E*>(a.Q) + base;
@@ -575,7 +642,9 @@ __global__ __launch_bounds__(NW * 64, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
     }
     if (qi < T && h == 0) b.Dw[size_t(bh) * size_t(T) + size_t(qi)] = Dq;
     const float lse2 = qi < T ? b.lse[size_t(bh) * size_t(T) + size_t(qi)] * kLog2e : 0.f;
-    const bool rowg = qi < T && ((a.rowbits[qi >> 5] >> (qi & 31)) & 1u);
+    // A 32-query group's global-row bits: one word, through the scalar cache.
+    const bool rowg =
+        qi < T && ((ldc(a.rowbits, min(qb * (NW * 32) + wave * 32, T - 1) >> 5) >> n) & 1u);
     const int qres = a.dil == 1 ? 0 : qi % a.dil;
     const int qblk = a.blk > 0 ? min(qi, T - 1) / a.blk : 0;
 
@@ -583,18 +652,20 @@ __global__ __launch_bounds__(NW * 64, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
 #pragma unroll
     for (int db = 0; db < S::NDB; ++db) acc[db] = f32x16{};
 
-    const int ga0 = ldc(a.gseg, 4 * it), ga1 = ldc(a.gseg, 4 * it + 1);
-    const int gb0 = ldc(a.gseg, 4 * it + 2), gb1 = ldc(a.gseg, 4 * it + 3);
+    const int ga0 = ldc(rec, REC_GA0), ga1 = ldc(rec, REC_GA1);
+    const int gb0 = ldc(rec, REC_GB0), gb1 = ldc(rec, REC_GB1);
     const int gna = ga1 - ga0, gtot = gna + (gb1 - gb0);
     auto gkey = [&](int slot) { return a.colkeys[slot < gna ? ga0 + slot : gb0 + (slot - gna)]; };
 
+    // Every row of the sequence lies in its T * D * 2 bytes (at most 1 GiB).
+    const DmaTile<D, NW> dt(wave, lane);
+    const __amdgpu_buffer_rsrc_t krs = raw_rsrc(Kp, T * D * 2), vrs = raw_rsrc(Vp, T * D * 2);
     auto issue = [&](const BwdCursor& c, E* kd, E* vd) {
         if (c.inplace()) {
-            const int k0 = c.kb * kBK;
-            dma_rows2<D, NW>(kd, vd, Kp, Vp, [&](int r) { return min(k0 + r, T - 1); }, wave, lane);
+            dt.rows_from(krs, vrs, kd, vd, c.kb * kBK, T);
         } else {
             const int g0 = c.gi;
-            dma_rows2<D, NW>(kd, vd, Kp, Vp, [&](int r) { return gkey(min(g0 + r, gtot - 1)); }, wave, lane);
+            dt.rows_listed(krs, vrs, kd, vd, [&](int r) { return gkey(min(g0 + r, gtot - 1)); });
         }
     };
     auto compute = [&](const BwdCursor& c, const E* kt, const E* vt) {
@@ -623,21 +694,56 @@ __global__ __launch_bounds__(NW * 64, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
     };
 
     // Tile t computes from slot t % 2 while tile t + 1 loads into the other.
-    BwdCursor cur{ldc(a.run_ptr, it), ldc(a.run_ptr, it + 1), 0, 0, false, 0, gtot};
-    bcur_enter(cur, a);
-    int slot = 0;
-    if (!cur.done()) issue(cur, kbuf, vbuf);
-    dma_tile_barrier();
-    while (!cur.done()) {
-        BwdCursor nxt = cur;
-        bcur_advance(nxt, a);
-        if (!nxt.done()) issue(nxt, kbuf + (slot ^ 1) * TILE, vbuf + (slot ^ 1) * TILE);
-        compute(cur, kbuf + slot * TILE, vbuf + slot * TILE);
+    const int first_end = ldc(rec, REC_FIRST_END);
+    BwdCursor cur{ldc(rec, REC_RUN_BEGIN), ldc(rec, REC_RUN_END), ldc(rec, REC_FIRST_KB),
+                  first_end & 0x7fffffff, first_end < 0, 0, gtot};
+    if constexpr (D == 64) {
+        // Two slots as distinct objects, indexed statically (the loop is
+        // unrolled by two), so the compiler can tell the prefetch into one
+        // from the reads of the other and keeps the prefetch in flight.
+        __shared__ __attribute__((aligned(1024))) E kbuf0[TILE];
+        __shared__ __attribute__((aligned(1024))) E vbuf0[TILE];
+        __shared__ __attribute__((aligned(1024))) E kbuf1[TILE];
+        __shared__ __attribute__((aligned(1024))) E vbuf1[TILE];
+        if (!cur.done()) issue(cur, kbuf0, vbuf0);
         dma_tile_barrier();
-        cur = nxt;
-        slot ^= 1;
+        while (!cur.done()) {
+            BwdCursor nxt = cur;
+            bcur_advance(nxt, a);
+            if (!nxt.done()) issue(nxt, kbuf1, vbuf1);
+            compute(cur, kbuf0, vbuf0);
+            dma_tile_barrier();
+            if (nxt.done()) break;
+            cur = nxt;
+            bcur_advance(nxt, a);
+            if (!nxt.done()) issue(nxt, kbuf0, vbuf0);
+            compute(cur, kbuf1, vbuf1);
+            dma_tile_barrier();
+            cur = nxt;
+        }
+    } else {
+        // d = 128 at two waves per SIMD has no registers for a second copy
+        // of the loop body (it spills 224 bytes): the slot is chosen at run
+        // time, and a tile's reads of its slot then also wait for the loads
+        // into the other one, which the second wave of the SIMD covers.  (One
+        // wave per SIMD with two static slots fits in 296 registers but
+        // measured 11% slower on the 32K window layer.)
+        __shared__ __attribute__((aligned(1024))) E kbuf[2 * TILE];
+        __shared__ __attribute__((aligned(1024))) E vbuf[2 * TILE];
+        int slot = 0;
+        if (!cur.done()) issue(cur, kbuf, vbuf);
+        dma_tile_barrier();
+        while (!cur.done()) {
+            BwdCursor nxt = cur;
+            bcur_advance(nxt, a);
+            if (!nxt.done()) issue(nxt, kbuf + (slot ^ 1) * TILE, vbuf + (slot ^ 1) * TILE);
+            compute(cur, kbuf + slot * TILE, vbuf + slot * TILE);
+            dma_tile_barrier();
+            cur = nxt;
+            slot ^= 1;
+        }
     }
-    const int part = a.item_part ? ldc(a.item_part, it) : -1;
+    const int part = ldc(rec, REC_PART);
     if (part >= 0)  // one key range of a split block: unscaled partial
         store_rows_f32<D>(b.dq_part + (size_t(bh) * a.n_parts + part) * (NW * 32) * D, acc,
                           qi - qb * (NW * 32), h);
