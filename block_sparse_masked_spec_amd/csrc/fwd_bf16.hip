@@ -7,11 +7,14 @@
 // is how a tile is fed to the matrix cores:
 //
 //   * a workgroup of NW wavefronts covers the query block (128 rows, or 64
-//     with two waves); each wave owns NG groups of 32 queries (one MFMA
-//     column block each).  The launches use NG = 1: a wave then needs at
-//     most 256 registers, so two waves share each SIMD and one wave's softmax
-//     can run while the other's matrix products do.  (NG = 2 would feed two
-//     MFMAs per fragment read but, at one wave per SIMD, measured slower);
+//     with two waves); each wave owns 32 queries.  At d = 64 they are one
+//     32-wide MFMA column block (v_mfma_f32_32x32x16_bf16, NG groups of 32;
+//     the launches use NG = 1).  At d = 128 they are two 16-query blocks of
+//     v_mfma_f32_16x16x32_bf16: the same work in twice as many MFMAs of half
+//     the length, which gives the scheduler finer interleave points (1-4%
+//     faster there; 5-15% slower at d = 64).  Either way a wave needs at most
+//     256 registers, so two waves share each SIMD and one wave's softmax can
+//     run while the other's matrix products do;
 //   * LDS holds each K and V tile "fragment-major": for every MFMA k-step,
 //     the 64 lanes' operand pieces are stored contiguously in lane order.
 //     Every fragment read is then lane_base + a compile-time offset and 32
@@ -22,7 +25,8 @@
 //   * two LDS buffers: tile t+1 is loaded while tile t is computed;
 //   * V^T fragments come from transposed LDS reads (ds_read_b64_tr_b16):
 //     within each 16-lane group, output lane j element e is element j%4 of
-//     the 8-byte piece addressed by lane 4e + j/4;
+//     the 8-byte piece addressed by lane 4e + j/4 (checked on the hardware,
+//     as are the 16x16x32 operand layouts and permlane16_swap's pairing);
 //   * the running max moves only when a score exceeds it by more than 2^8
 //     (log2 domain), so the accumulator rescale is almost never paid --
 //     exact either way, since every weight of a row uses the same reference;
@@ -35,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "internal.hpp"
 #include "kernel_common.hpp"
 
@@ -46,6 +52,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 static_assert(sizeof(i32x16) == sizeof(int32_t) * kItemRec, "one item record");
 
@@ -61,28 +68,20 @@ static_assert(kBK == 64, "one column-bit word per key tile");
 
 __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-template <int D, int NW>
+// Tile shapes.  M16 selects the 16x16x32 MFMA (v_mfma_f32_16x16x32_bf16,
+// used at d = 128), else the 32x32x16 one (d = 64); both run 2 products of
+// the same cost per tile, with different fragment layouts.
+template <int D, int NW, bool M16>
 struct Lay {
-    static constexpr int TILE = kBK * D * 2;          // bytes per K or V tile
-    static constexpr int LOADS = TILE / 1024;         // 1 KiB wave-wide loads per tile
+    static constexpr int TILE = kBK * D * 2;           // bytes per K or V tile
+    static constexpr int LOADS = TILE / 1024;          // 1 KiB wave-wide loads per tile
     static constexpr int LOADS_PER_WAVE = LOADS / NW;
-    static constexpr int NKS = D / 16;                // k-steps of S^T = K Q^T
-    static constexpr int NDB = D / 32;                // 32-row blocks of O^T
-    static_assert(LOADS == 2 * NKS && LOADS == 4 * NDB, "one 1 KiB block per k-step pair");
+    static constexpr int NKS = M16 ? D / 32 : D / 16;  // k-steps of S^T = K Q^T
+    static constexpr int NDB = M16 ? D / 16 : D / 32;  // row blocks of O^T
+    static constexpr int NKB = M16 ? 4 : 2;            // key blocks of a tile (16 or 32 keys)
+    static_assert(LOADS == NKB * NKS && LOADS == (M16 ? 2 : 4) * NDB, "one 1 KiB block per fragment");
     static_assert(LOADS % NW == 0, "loads split evenly over the waves");
 };
-
-// K tile layout: 1 KiB block (b, ks) = b * NKS + ks holds, at byte lane*16,
-// the A fragment of lane (n = lane%32, h = lane/32) for key block b and
-// k-step ks: K[b*32 + swap23(n)][ks*16 + h*8 .. +8].  Rows enter the MFMA in
-// swap23 order so that a lane's 8 scores of one PV k-step are 8 consecutive
-// keys (register r of block b then holds key b*32 + (r/8)*16 + h*8 + r%8).
-//
-// V tile layout: 1 KiB block (kk, db) = kk * NDB + db holds two 512-byte
-// halves rd = 0, 1; transposed-read lane l reads 8 bytes at rd*512 + l*8:
-// V[kk*16 + h*8 + (l%16)/4 + 4*rd][db*32 + ((l/16)%2)*16 + (l%4)*4 .. +4].
-// After the transposed read, lane (n, h) holds V^T[db*32 + n][kk*16 + h*8 +
-// e] for e = 0..7 (rd = 0 gives e < 4) -- the A fragment of O^T += V^T P^T.
 
 // Where the next tile comes from: a run of in-place key tiles or a slice of
 // the gathered column keys.
@@ -121,22 +120,62 @@ __device__ __forceinline__ uint64_t rule_word(const FwdArgs& a, int qi, int k0, 
     return allowed_word(a, qi, k0, rowg, ldc(a.colbits, k0 >> 6), qres, k0res, qblk);
 }
 
+// 32x32x16 K tile layout: 1 KiB block (b, ks) = b * NKS + ks holds, at byte lane*16,
+// the A fragment of lane (n = lane%32, h = lane/32) for key block b and
+// k-step ks: K[b*32 + swap23(n)][ks*16 + h*8 .. +8].  Rows enter the MFMA in
+// swap23 order so that a lane's 8 scores of one PV k-step are 8 consecutive
+// keys (register r of block b then holds key b*32 + (r/8)*16 + h*8 + r%8).
+//
+// 32x32x16 V tile layout: 1 KiB block (kk, db) = kk * NDB + db holds two 512-byte
+// halves rd = 0, 1; transposed-read lane l reads 8 bytes at rd*512 + l*8:
+// V[kk*16 + h*8 + (l%16)/4 + 4*rd][db*32 + ((l/16)%2)*16 + (l%4)*4 .. +4].
+// After the transposed read, lane (n, h) holds V^T[db*32 + n][kk*16 + h*8 +
+// e] for e = 0..7 (rd = 0 gives e < 4) -- the A fragment of O^T += V^T P^T.
+
+// 16x16x32 K tile layout: 1 KiB block (kb, ks) = kb * NKS + ks holds lane
+// l's A fragment, K[row(kb, l%16)][ks*32 + 8*(l/16) .. +8], with row(kb, r)
+// = (kb/2)*32 + 8*(r/4) + 4*(kb%2) + r%4: the four score rows that lane group
+// g = l/16 holds of blocks 2kk and 2kk+1 are then keys kk*32 + 8g .. +8, the
+// B fragment of the PV product for that 32-key step.
+//
+// 16x16x32 V tile layout: 1 KiB block (kk, db) = kk * NDB + db holds two
+// 512-byte halves rd; transposed-read lane l = 16g + 4e + q reads 8 bytes at
+// rd*512 + l*8: V[kk*32 + 8g + 4rd + e][db*16 + 4q .. +4].  After the two
+// transposed reads lane (16g + j) holds V^T[db*16 + j][kk*32 + 8g + e], e =
+// 0..7 -- the A fragment of O^T += V^T P^T.
+
 // Tile row (key slot 0..63) that load gi of a tile, lane `lane`, copies, and
 // the element offset within that key's row.
-template <int D>
+template <int D, bool M16>
 __device__ __forceinline__ void k_piece(int gi, int lane, int* row, int* col) {
-    constexpr int NKS = D / 16;
-    *row = (gi / NKS) * 32 + swap23(lane & 31);
-    *col = (gi % NKS) * 16 + (lane >> 5) * 8;
+    if constexpr (M16) {
+        constexpr int NKS = D / 32;
+        const int kb = gi / NKS, ks = gi % NKS, r = lane & 15;
+        *row = (kb >> 1) * 32 + 8 * (r >> 2) + 4 * (kb & 1) + (r & 3);
+        *col = ks * 32 + 8 * (lane >> 4);
+    } else {
+        constexpr int NKS = D / 16;
+        *row = (gi / NKS) * 32 + swap23(lane & 31);
+        *col = (gi % NKS) * 16 + (lane >> 5) * 8;
+    }
 }
-template <int D>
+template <int D, bool M16>
 __device__ __forceinline__ void v_piece(int gi, int lane, int* row, int* col) {
-    constexpr int NDB = D / 32;
-    const int kk = gi / NDB, db = gi % NDB;
-    const int rd = lane >> 5, l0 = 2 * (lane & 31);
-    const int g = l0 >> 4, L = l0 & 15, h = l0 >> 5;
-    *row = kk * 16 + h * 8 + (L >> 2) + 4 * rd;
-    *col = db * 32 + (g & 1) * 16 + (L & 3) * 4;
+    if constexpr (M16) {
+        constexpr int NDB = D / 16;
+        const int kk = gi / NDB, db = gi % NDB;
+        const int rd = lane >> 5, l0 = 2 * (lane & 31);
+        const int g = l0 >> 4, e = (l0 & 15) >> 2, q = l0 & 3;
+        *row = kk * 32 + 8 * g + 4 * rd + e;
+        *col = db * 16 + 4 * q;
+    } else {
+        constexpr int NDB = D / 32;
+        const int kk = gi / NDB, db = gi % NDB;
+        const int rd = lane >> 5, l0 = 2 * (lane & 31);
+        const int g = l0 >> 4, L = l0 & 15, h = l0 >> 5;
+        *row = kk * 16 + h * 8 + (L >> 2) + 4 * rd;
+        *col = db * 32 + (g & 1) * 16 + (L & 3) * 4;
+    }
 }
 
 // The direct loads of one K tile and one V tile (this wave's share), as
@@ -151,9 +190,9 @@ __device__ __forceinline__ void v_piece(int gi, int lane, int* row, int* col) {
 // inherit the wait on the gathered path's key reads -- and, since vector
 // loads complete in order, on every load in flight.  The marker after each
 // path's loads keeps the compiler from merging them.
-template <int D, int NW>
+template <int D, int NW, bool M16>
 struct TileLoad {
-    using L = Lay<D, NW>;
+    using L = Lay<D, NW, M16>;
     __amdgpu_buffer_rsrc_t krsrc, vrsrc;
     int rowb;                                  // bytes between key rows
     int wave;
@@ -172,8 +211,8 @@ struct TileLoad {
         for (int i = 0; i < L::LOADS_PER_WAVE; ++i) {
             const int gi = wave * L::LOADS_PER_WAVE + i;
             int kc, vc;
-            k_piece<D>(gi, lane, &kr[i], &kc);
-            v_piece<D>(gi, lane, &vr[i], &vc);
+            k_piece<D, M16>(gi, lane, &kr[i], &kc);
+            v_piece<D, M16>(gi, lane, &vr[i], &vc);
             koff[i] = kr[i] * rowb + kc * 2;
             voff[i] = vr[i] * rowb + vc * 2;
         }
@@ -233,12 +272,50 @@ __device__ __forceinline__ void tile_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// 32x32x16 tiles: the wave's queries as NG groups of 32, one per lane column
+// (lane l holds query l%32 of each group).
 template <int D, int NG, int NW>
 struct WaveState {
-    using L = Lay<D, NW>;
+    using L = Lay<D, NW, false>;
+    static constexpr int NQ = NG;     // queries per lane
+    static constexpr int SLOT = 32;   // queries per group
     bf16x8 qf[NG][L::NKS];   // Q^T fragments of the wave's query groups
     f32x16 acc[NG][L::NDB];  // O^T accumulators
     float m_run[NG], l_run[NG];
+
+    static __device__ __forceinline__ int query(int lane) { return lane & 31; }
+    // one lane per query writes the row's LSE or partial max and sum
+    static __device__ __forceinline__ bool owns_row(int lane) { return lane < 32; }
+    __device__ __forceinline__ void load_q(int g, const __bf16* Qp, int qi, size_t rs, int T, int lane) {
+#pragma unroll
+        for (int ks = 0; ks < L::NKS; ++ks) {
+            qf[g][ks] = bf16x8{};
+            if (qi < T) qf[g][ks] = *reinterpret_cast<const bf16x8*>(Qp + size_t(qi) * rs + ks * 16 + (lane >> 5) * 8);
+        }
+#pragma unroll
+        for (int db = 0; db < L::NDB; ++db) acc[g][db] = f32x16{};
+        m_run[g] = -1e30f;
+        l_run[g] = 0.f;
+    }
+    // l over both lane halves
+    __device__ __forceinline__ float row_sum(int g) const {
+        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[g]), __float_as_uint(l_run[g]),
+                                                         false, false);
+        return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+    }
+    // f(d0, four accumulator values of output columns d0 .. d0+3)
+    template <typename F>
+    __device__ __forceinline__ void outputs(int g, int lane, F f) const {
+#pragma unroll
+        for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[g][db][r4 * 4 + e];
+                f(db * 32 + r4 * 8 + (lane >> 5) * 4, v);
+            }
+    }
 
     // One 64-key tile.  With `masked`, allowed[g] has bit k set iff key k of
     // the tile is allowed for this lane's query of group g.
@@ -352,6 +429,145 @@ struct WaveState {
     }
 };
 
+// 16x16x32 tiles: the wave's 32 queries as two blocks of 16; lane l holds
+// query l%16 of each block, and lane group g = l/16 holds score rows 4g ..
+// 4g+3 of each 16-key block (keys of the tile as the K layout orders them).
+template <int D, int NW>
+struct WaveState16 {
+    using L = Lay<D, NW, true>;
+    static constexpr int NQ = 2;      // queries per lane
+    static constexpr int SLOT = 16;   // queries per block
+    bf16x8 qf[NQ][L::NKS];   // Q^T fragments (B operands)
+    f32x4 acc[L::NDB][NQ];   // O^T accumulators
+    float m_run[NQ], l_run[NQ];
+
+    static __device__ __forceinline__ int query(int lane) { return lane & 15; }
+    static __device__ __forceinline__ bool owns_row(int lane) { return lane < 16; }
+    __device__ __forceinline__ void load_q(int qh, const __bf16* Qp, int qi, size_t rs, int T, int lane) {
+#pragma unroll
+        for (int ks = 0; ks < L::NKS; ++ks) {
+            qf[qh][ks] = bf16x8{};
+            if (qi < T) qf[qh][ks] = *reinterpret_cast<const bf16x8*>(Qp + size_t(qi) * rs + ks * 32 + (lane >> 4) * 8);
+        }
+#pragma unroll
+        for (int db = 0; db < L::NDB; ++db) acc[db][qh] = f32x4{};
+        m_run[qh] = -1e30f;
+        l_run[qh] = 0.f;
+    }
+    // l over the four lane groups that share the query
+    __device__ __forceinline__ float row_sum(int qh) const {
+        const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(l_run[qh]), __float_as_uint(l_run[qh]),
+                                                          false, false);
+        const float x = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+        const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+    }
+    template <typename F>
+    __device__ __forceinline__ void outputs(int qh, int lane, F f) const {
+#pragma unroll
+        for (int db = 0; db < L::NDB; ++db) f(db * 16 + (lane >> 4) * 4, acc[db][qh]);
+    }
+
+    // One 64-key tile.  With `masked`, allowed[qh] has bit k set iff key k
+    // of the tile is allowed for this lane's query of block qh.
+    __device__ __forceinline__ void tile(const char* kt, const char* vt, const FwdArgs& a, int lane,
+                                         bool masked, const uint64_t (&allowed)[NQ]) {
+        const int g = lane >> 4;
+        f32x4 s[4][NQ];  // [16-key block][query block]
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int qh = 0; qh < NQ; ++qh) s[kb][qh] = f32x4{};
+        // S^T = K Q^T: each K fragment feeds both query blocks.  All of the
+        // tile's K fragments are read first, then the MFMAs run.
+        bf16x8 kfa[4 * L::NKS];
+#pragma unroll
+        for (int i = 0; i < 4 * L::NKS; ++i) kfa[i] = *reinterpret_cast<const bf16x8*>(kt + i * 1024 + lane * 16);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4 * L::NKS; ++i)
+#pragma unroll
+            for (int qh = 0; qh < NQ; ++qh)
+                s[i / L::NKS][qh] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfa[i], qf[qh][i % L::NKS], s[i / L::NKS][qh], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // Every V^T fragment of the tile, read while the softmax runs.
+        bf16x8 vfa[2 * L::NDB];
+#pragma unroll
+        for (int i = 0; i < 2 * L::NDB; ++i) {
+            const char* blk = vt + i * 1024 + lane * 8;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(blk));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds_s16x4(blk + 512));
+            vfa[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 pf[NQ][2];  // [query block][32-key step]
+#pragma unroll
+        for (int qh = 0; qh < NQ; ++qh) {
+            if (masked) {
+                // score t of block kb is key (kb/2)*32 + 8g + 4*(kb%2) + t
+                const uint64_t mine = allowed[qh] >> (8 * g);
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int bit = (kb >> 1) * 32 + 4 * (kb & 1) + t;
+                        if (!((mine >> bit) & 1)) s[kb][qh][t] = -INFINITY;
+                    }
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) mx = fmaxf(mx, s[kb][qh][t]);
+            {  // over the four lane groups of the query
+                const auto p16 =
+                    __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mx = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+                const auto p32 =
+                    __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mx = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+            }
+            const float ms = mx * a.scale_log2;
+            if (__any(ms > m_run[qh] + kLazyTau)) {
+                const float m_new = fmaxf(m_run[qh], ms);
+                const float alpha = __builtin_amdgcn_exp2f(m_run[qh] - m_new);
+                m_run[qh] = m_new;
+                l_run[qh] *= alpha;
+#pragma unroll
+                for (int db = 0; db < L::NDB; ++db) acc[db][qh] *= alpha;
+            }
+            const float mneg = -m_run[qh];
+            bf16x2 ones;
+            ones[0] = static_cast<__bf16>(1.0f);
+            ones[1] = static_cast<__bf16>(1.0f);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pf[qh][kk][e] = static_cast<__bf16>(
+                        __builtin_amdgcn_exp2f(fmaf(s[2 * kk + (e >> 2)][qh][e & 3], a.scale_log2, mneg)));
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    bf16x2 pair;
+                    pair[0] = pf[qh][kk][e];
+                    pair[1] = pf[qh][kk][e + 1];
+                    l_run[qh] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_run[qh], false);
+                }
+            }
+        }
+        // O^T += V^T P^T: each V^T fragment feeds both query blocks.
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int db = 0; db < L::NDB; ++db)
+#pragma unroll
+                for (int qh = 0; qh < NQ; ++qh)
+                    acc[db][qh] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfa[kk * L::NDB + db], pf[qh][kk], acc[db][qh], 0, 0, 0);
+    }
+};
+
 // Waves per SIMD to ask the compiler for: two when a wave holds one query
 // group (fits in 256 registers), else one.
 template <int NG>
@@ -363,12 +579,17 @@ template <int D, int NG, int NW, bool SUB>
 __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_bf16_kernel(FwdArgs a) {
     constexpr int BQ = NW * NG * 32;  // waves x groups x 32 queries = one query block
     static_assert(BQ == kBQ || BQ == 64, "query blocks of the plans: 128 or 64 rows");
-    using L = Lay<D, NW>;
+    // d = 128 runs the 16x16x32 tiles (measured 1-4% faster there), d = 64
+    // the 32x32x16 ones (the 16x16x32 form measured 5-15% slower at d = 64).
+    constexpr bool M16 = D == 128;
+    static_assert(!M16 || NG == 1, "16x16x32 tiles: 32 queries per wave");
+    using L = Lay<D, NW, M16>;
+    using WS = std::conditional_t<M16, WaveState16<D, NW>, WaveState<D, NG, NW>>;
+    constexpr int NQ = WS::NQ;
 
     // The wave index is uniform across the wave; readfirstlane lets the
     // compiler keep it, and every address derived from it, in scalar registers.
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n = lane & 31, h = lane >> 5;
     const int work = xcd_slice_index(blockIdx.x, gridDim.x);
     const int n_items = gridDim.x / a.BH;
     const int bh = work / n_items;
@@ -387,31 +608,24 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
     const __bf16* Vp = static_cast<const __bf16*>(a.V) + base;
     __bf16* Op = static_cast<__bf16*>(a.O) + base;
     const int q_base = qb * BQ + wave * NG * 32;
-    const TileLoad<D, NW> ld(Kp, Vp, T, rs, wave, lane);
+    const TileLoad<D, NW, M16> ld(Kp, Vp, T, rs, wave, lane);
 
-    WaveState<D, NG, NW> st;
-    bool rowg[NG];
-    int qres[NG];  // query index mod the dilation
-    int qblk[NG];  // block mode: the query's block (padding rows use the last row's)
+    // Lane `lane` holds query qi(x) of each of its NQ query slots.
+    auto qi_of = [&](int x) { return q_base + x * WS::SLOT + WS::query(lane); };
+    WS st;
+    bool rowg[NQ];
+    int qres[NQ];  // query index mod the dilation
+    int qblk[NQ];  // block mode: the query's block (padding rows use the last row's)
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        const int qi = q_base + g * 32 + n;
-#pragma unroll
-        for (int ks = 0; ks < L::NKS; ++ks) {
-            st.qf[g][ks] = bf16x8{};
-            if (qi < T)
-                st.qf[g][ks] = *reinterpret_cast<const bf16x8*>(Qp + size_t(qi) * rs + ks * 16 + h * 8);
-        }
-#pragma unroll
-        for (int db = 0; db < L::NDB; ++db) st.acc[g][db] = f32x16{};
-        st.m_run[g] = -1e30f;
-        st.l_run[g] = 0.f;
-        // A group's 32 queries share one word of the global-row bits (read
+    for (int x = 0; x < NQ; ++x) {
+        const int qi = qi_of(x);
+        st.load_q(x, Qp, qi, rs, T, lane);
+        // A slot's queries share one word of the global-row bits (read
         // through the scalar cache, so it adds no wait on the Q loads).
-        const uint32_t rw = ldc(a.rowbits, min(q_base + g * 32, T - 1) >> 5);
-        rowg[g] = qi < T && ((rw >> n) & 1u);
-        qres[g] = a.dil == 1 ? 0 : qi % a.dil;
-        qblk[g] = a.blk > 0 ? min(qi, T - 1) / a.blk : 0;
+        const uint32_t rw = ldc(a.rowbits, min(q_base + x * WS::SLOT, T - 1) >> 5);
+        rowg[x] = qi < T && ((rw >> (qi & 31)) & 1u);
+        qres[x] = a.dil == 1 ? 0 : qi % a.dil;
+        qblk[x] = a.blk > 0 ? min(qi, T - 1) / a.blk : 0;
     }
 
     const int ga0 = rec[REC_GA0], gna = rec[REC_GA1] - ga0, gb0 = rec[REC_GB0];
@@ -420,14 +634,13 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
 
     auto run_tile = [&](const Cursor& c, const char* kt, const char* vt) {
         const bool masked = !c.inplace() || c.masked;
-        uint64_t allowed[NG];
+        uint64_t allowed[NQ];
         const int k0res = a.dil == 1 ? 0 : (c.kb * kBK) % a.dil;
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            allowed[g] = ~0ull;
+        for (int x = 0; x < NQ; ++x) {
+            allowed[x] = ~0ull;
             if (masked)
-                allowed[g] = c.inplace() ? rule_word(a, q_base + g * 32 + n, c.kb * kBK, rowg[g],
-                                                     qres[g], k0res, qblk[g])
+                allowed[x] = c.inplace() ? rule_word(a, qi_of(x), c.kb * kBK, rowg[x], qres[x], k0res, qblk[x])
                                          : low_bits(min(kBK, c.g_total - c.gi));
         }
         st.tile(kt, vt, a, lane, masked, allowed);
@@ -458,56 +671,47 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
         cur = nxt;
     }
 
-    // Epilogue: O = acc / l (both lane halves' sums), or -- for one part of
-    // a split block -- acc, the running max and l into the item's slot.
+    // Epilogue: O = acc / l (l summed over the lanes that share the query),
+    // or -- for one part of a split block -- acc, the running max and l into
+    // the item's slot.
     const int part = rec[REC_PART];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        const int qi = q_base + g * 32 + n;
-        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.l_run[g]),
-                                                         __float_as_uint(st.l_run[g]), false, false);
-        const float lt = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+    for (int x = 0; x < NQ; ++x) {
+        const int qi = qi_of(x);
+        const float lt = st.row_sum(x);
         if (part >= 0) {
             const size_t slot = (size_t(bh) * a.n_parts + part) * BQ + (qi - qb * BQ);
             float* po = a.part + slot * D;
-#pragma unroll
-            for (int db = 0; db < L::NDB; ++db)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    float4 q;
-                    q.x = st.acc[g][db][r4 * 4];
-                    q.y = st.acc[g][db][r4 * 4 + 1];
-                    q.z = st.acc[g][db][r4 * 4 + 2];
-                    q.w = st.acc[g][db][r4 * 4 + 3];
-                    *reinterpret_cast<float4*>(po + db * 32 + r4 * 8 + h * 4) = q;
-                }
-            if (h == 0) {
+            st.outputs(x, lane, [&](int d0, const f32x4& v) {
+                float4 q;
+                q.x = v[0];
+                q.y = v[1];
+                q.z = v[2];
+                q.w = v[3];
+                *reinterpret_cast<float4*>(po + d0) = q;
+            });
+            if (WS::owns_row(lane)) {
                 float2 ml;
-                ml.x = st.m_run[g];
+                ml.x = st.m_run[x];
                 ml.y = lt;
                 reinterpret_cast<float2*>(a.part + size_t(a.BH) * a.n_parts * BQ * D)[slot] = ml;
             }
             continue;
         }
         const float inv = 1.f / lt;
-        if (a.lse && qi < T && h == 0) {  // log-sum-exp: the scores are in log2 units
+        if (a.lse && qi < T && WS::owns_row(lane)) {  // log-sum-exp: the scores are in log2 units
             const size_t row = SUB ? size_t(bh / a.sub) * size_t(T) * a.sub + size_t(bh % a.sub) +
                                          size_t(qi) * a.sub
                                    : size_t(bh) * size_t(T) + size_t(qi);
-            a.lse[row] = (st.m_run[g] + __log2f(lt)) * 0.6931471805599453f;
+            a.lse[row] = (st.m_run[x] + __log2f(lt)) * 0.6931471805599453f;
         }
-        if (qi < T) {
+        if (qi < T)
+            st.outputs(x, lane, [&](int d0, const f32x4& v) {
+                bf16x4 q;
 #pragma unroll
-            for (int db = 0; db < L::NDB; ++db)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int d0 = db * 32 + r4 * 8 + h * 4;
-                    bf16x4 q;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) q[e] = static_cast<__bf16>(st.acc[g][db][r4 * 4 + e] * inv);
-                    *reinterpret_cast<bf16x4*>(Op + size_t(qi) * rs + d0) = q;
-                }
-        }
+                for (int e = 0; e < 4; ++e) q[e] = static_cast<__bf16>(v[e] * inv);
+                *reinterpret_cast<bf16x4*>(Op + size_t(qi) * rs + d0) = q;
+            });
     }
 }
 
