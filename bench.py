@@ -70,6 +70,11 @@ WORKLOADS = {
 }
 DEFAULT_WORKLOAD = "mistral32k_window4096"
 ROTATE_BYTES = 512 << 20  # input copies touched per pass: above twice the 256 MB MALL
+# At most this many copies: a workload under ROTATE_BYTES / MAX_COPIES (the
+# 16-token case, 4 KiB) is bound by launch latency, not by where its bytes
+# sit, and its 131,072 copies would only add half a million clone kernels
+# to every profile of the run.
+MAX_COPIES = 64
 
 
 def kernel_source(wl) -> str:
@@ -541,14 +546,15 @@ def main():
     # Inputs: one fresh seeded set per call of the step (the interleave
     # workload runs several independent calls), resident on the GPU.  Small
     # workloads rotate over enough copies that one pass touches more than
-    # twice the 256 MB last-level cache, so each step reads HBM, not cache.
+    # twice the 256 MB last-level cache, so each step reads HBM, not cache
+    # (up to MAX_COPIES).
     host_sets, dev_sets = [], []
     for c, spec in enumerate(specs):
         q, k, v = inputs.qkv(B, H, T, d, dtype, args.seed + c)
         host_sets.append((q, k, v))
         dev_sets.append((q.cuda(), k.cuda(), v.cuda(), torch.empty_like(q, device="cuda")))
     set_bytes = 4 * q.numel() * q.element_size() * len(specs)
-    n_copies = max(1, -(-ROTATE_BYTES // set_bytes))
+    n_copies = min(MAX_COPIES, max(1, -(-ROTATE_BYTES // set_bytes)))
     copies = [dev_sets] + [[tuple(t.clone() for t in ds) for ds in dev_sets] for _ in range(n_copies - 1)]
     allowed = [sa.sparse_attn_count(s, T) for s in specs]
     E_total = sum(allowed) * B * H  # allowed (b,h,i,j) pairs per step
