@@ -429,13 +429,14 @@ struct WaveState {
     }
 };
 
-// 16x16x32 tiles: the wave's 32 queries as two blocks of 16; lane l holds
-// query l%16 of each block, and lane group g = l/16 holds score rows 4g ..
-// 4g+3 of each 16-key block (keys of the tile as the K layout orders them).
-template <int D, int NW>
+// 16x16x32 tiles: the wave's queries as NQB blocks of 16 (two at d = 128;
+// one in the 16-query waves of small grids); lane l holds query l%16 of
+// each block, and lane group g = l/16 holds score rows 4g .. 4g+3 of each
+// 16-key block (keys of the tile as the K layout orders them).
+template <int D, int NW, int NQB>
 struct WaveState16 {
     using L = Lay<D, NW, true>;
-    static constexpr int NQ = 2;      // queries per lane
+    static constexpr int NQ = NQB;    // queries per lane (16-query blocks per wave)
     static constexpr int SLOT = 16;   // queries per block
     bf16x8 qf[NQ][L::NKS];   // Q^T fragments (B operands)
     f32x4 acc[L::NDB][NQ];   // O^T accumulators
@@ -575,16 +576,20 @@ struct Occupancy {
     static constexpr int kWavesPerSimd = NG == 1 ? 2 : 1;
 };
 
-template <int D, int NG, int NW, bool SUB>
+// QW: queries per wave.  32: NG groups of 32 (d = 64) or two 16-query
+// blocks (d = 128); 16: one 16-query block per wave, for grids too small to
+// give each SIMD two waves otherwise (eight waves cover a 128-query block).
+template <int D, int NG, int NW, bool SUB, int QW>
 __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_bf16_kernel(FwdArgs a) {
-    constexpr int BQ = NW * NG * 32;  // waves x groups x 32 queries = one query block
+    constexpr int BQ = NW * NG * QW;  // waves x queries per wave = one query block
     static_assert(BQ == kBQ || BQ == 64, "query blocks of the plans: 128 or 64 rows");
     // d = 128 runs the 16x16x32 tiles (measured 1-4% faster there), d = 64
-    // the 32x32x16 ones (the 16x16x32 form measured 5-15% slower at d = 64).
-    constexpr bool M16 = D == 128;
-    static_assert(!M16 || NG == 1, "16x16x32 tiles: 32 queries per wave");
+    // the 32x32x16 ones (the 16x16x32 form measured 5-15% slower at d = 64)
+    // except in the 16-query waves.
+    constexpr bool M16 = D == 128 || QW == 16;
+    static_assert(!M16 || NG == 1, "16x16x32 tiles: one query group per wave");
     using L = Lay<D, NW, M16>;
-    using WS = std::conditional_t<M16, WaveState16<D, NW>, WaveState<D, NG, NW>>;
+    using WS = std::conditional_t<M16, WaveState16<D, NW, QW / 16>, WaveState<D, NG, NW>>;
     constexpr int NQ = WS::NQ;
 
     // The wave index is uniform across the wave; readfirstlane lets the
@@ -607,7 +612,7 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
     const __bf16* Kp = static_cast<const __bf16*>(a.K) + base;
     const __bf16* Vp = static_cast<const __bf16*>(a.V) + base;
     __bf16* Op = static_cast<__bf16*>(a.O) + base;
-    const int q_base = qb * BQ + wave * NG * 32;
+    const int q_base = qb * BQ + wave * NG * QW;
     const TileLoad<D, NW, M16> ld(Kp, Vp, T, rs, wave, lane);
 
     // Lane `lane` holds query qi(x) of each of its NQ query slots.
@@ -766,9 +771,13 @@ __global__ __launch_bounds__(256) void sa_fwd_merge_kernel(FwdArgs a, const int3
     if (a.lse && c == 0) a.lse[size_t(bh) * T + qi] = (m + __log2f(l)) * 0.6931471805599453f;
 }
 
-template <int D, int NG, int NW, bool SUB = false>
+#ifndef SA_FWD_SMALL_GRID
+#define SA_FWD_SMALL_GRID 512
+#endif
+
+template <int D, int NG, int NW, bool SUB = false, int QW = 32>
 int launch_t(const FwdArgs& a, int64_t grid, void* stream) {
-    hipLaunchKernelGGL((sa_fwd_bf16_kernel<D, NG, NW, SUB>), dim3(static_cast<unsigned>(grid)),
+    hipLaunchKernelGGL((sa_fwd_bf16_kernel<D, NG, NW, SUB, QW>), dim3(static_cast<unsigned>(grid)),
                        dim3(NW * 64), 0, static_cast<hipStream_t>(stream), a);
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
@@ -804,6 +813,7 @@ int launch_fwd_fast(int dtype, int d, const FwdArgs& a, int64_t grid, void* stre
     }
     if (a.bq == 64) return d == 64 ? launch_t<64, 1, 2>(a, grid, stream) : SA_ERR_UNSUPPORTED;
     if (d == 128) return launch_t<128, 1, 4>(a, grid, stream);
+    if (d == 64 && grid <= SA_FWD_SMALL_GRID) return launch_t<64, 1, 8, false, 16>(a, grid, stream);
     if (d == 64) return launch_t<64, 1, 4>(a, grid, stream);
     return SA_ERR_UNSUPPORTED;
 }
