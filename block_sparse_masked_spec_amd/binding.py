@@ -31,7 +31,7 @@ SA_ERR_HIP = -7
 SA_ERR_ALIGN = -8
 SA_ERR_NOMEM = -9
 SA_ERR_SCRATCH = -10
-SA_DECODE_SCRATCH_BYTES = 16 << 20
+SA_DECODE_SCRATCH_BYTES = 4 << 20
 
 SA_TILE_EMPTY, SA_TILE_FULL, SA_TILE_PARTIAL = 0, 1, 2
 SA_DTYPE_BF16, SA_DTYPE_F32 = 0, 1

@@ -652,12 +652,15 @@ int decode_prepare(const void* Q, const void* K, const void* V, void* O, const i
     a.reach = sa::band_reach32(m);
     a.dil = m.dilation > 1 ? m.dilation : 1;
     a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
-    // Key splits: enough workgroups to cover the chip (about 2048), each
-    // with at least 256 keys.
+    // Key splits: enough workgroups to fill the chip once -- 512, two per
+    // CU, what the kernel keeps resident at d = 128 -- each with at least 256
+    // keys. More splits only add rounds of workgroups, partial rows and the
+    // merge: at 64 sequences x 8 KV heads (512 groups, no split) decode
+    // streams 5.45 TB/s against 4.87 with four splits each.
     int64_t keys = min_rows > 0 ? std::min<int64_t>(C, min_rows) : C;
     if (n_new == 1 && a.dil > 1) keys = (keys + a.dil - 1) / a.dil;
     const int64_t groups = int64_t(B) * Hkv * nqchunks;
-    int64_t nsplit = (2048 + groups - 1) / groups;
+    int64_t nsplit = (512 + groups - 1) / groups;
     nsplit = std::max<int64_t>(1, std::min<int64_t>(nsplit, (keys + 255) / 256));
     a.nsplit = static_cast<int32_t>(nsplit);
     *part_bytes = a.nsplit > 1 ? size_t(B) * H * n_new * size_t(a.nsplit) * (d + 2) * sizeof(float) : 0;

@@ -310,13 +310,13 @@ int sparse_attn_decode(const void* Q, const void* K_cache, const void* V_cache, 
  * on this entry point's first call on that device.
  *
  * A call needs B * H * n_new * nsplit * (d + 2) * 4 bytes of scratch when it
- * splits the cache over nsplit > 1 workgroups (nsplit = ceil(2048 / groups)
- * for groups = B * Hkv * ceil(H / Hkv * n_new / 8) below 2048, capped so each
+ * splits the cache over nsplit > 1 workgroups (nsplit = ceil(512 / groups)
+ * for groups = B * Hkv * ceil(H / Hkv * n_new / 8) below 512, capped so each
  * split covers at least 256 keys; one split needs none).  That is at most
- * about 17 MB (d = 128, groups just below 2048); a call that needs more than
- * SA_DECODE_SCRATCH_BYTES (16 MiB) returns SA_ERR_SCRATCH before any device
- * work -- for example B = 255, H = 64, Hkv = 8, n_new = 1, d = 128 with a
- * 4096-row window -- and can use sparse_attn_decode instead.  Every partial a call reads is written by the same call first, so
+ * about 4.3 MB (d = 128, groups just below 512, eight queries each); a call
+ * that needs more than SA_DECODE_SCRATCH_BYTES (4 MiB) returns SA_ERR_SCRATCH
+ * before any device work -- for example B = 511, H = 8, Hkv = 1, n_new = 1,
+ * d = 128 with a 4096-row window -- and can use sparse_attn_decode instead.  Every partial a call reads is written by the same call first, so
  * nothing has to start at zero.
  *
  * All calls on one GPU share that GPU's array: calls on one stream are
@@ -324,7 +324,7 @@ int sparse_attn_decode(const void* Q, const void* K_cache, const void* V_cache, 
  * or several host threads without a common stream) race on it and must not
  * be issued.
  */
-#define SA_DECODE_SCRATCH_BYTES (16 << 20)
+#define SA_DECODE_SCRATCH_BYTES (4 << 20)
 int sparse_attn_decode_noalloc(const void* Q, const void* K_cache, const void* V_cache, void* O,
                                const int32_t* pos, int B, int H, int Hkv, int n_new, int C,
                                int d, const char* mask_spec, void* stream);

@@ -474,9 +474,9 @@ def test_noalloc_decode_checks_before_any_device_work():
     assert dec(Q, K, V, O, P, 2, 8, 2, 1, 100, 128, w, None) == sa.SA_ERR_SHAPE
     assert dec(Q, K, V, O, P, 2, 8, 2, 1, 4096, 48, w, None) == sa.SA_ERR_UNSUPPORTED
     assert dec(Q, K, V, O, P, 2, 8, 2, 1, 4096, 128, b"causal;stride=4", None) == sa.SA_ERR_UNSUPPORTED
-    # 255 x 8 groups get 2 key splits: 255*64*2*130*4 = 16.97 MB > 16 MiB
-    assert 255 * 64 * 2 * 130 * 4 > sa.SA_DECODE_SCRATCH_BYTES
-    assert dec(Q, K, V, O, P, 255, 64, 8, 1, 4096, 128, w, None) == sa.SA_ERR_SCRATCH
+    # 511 groups of 8 queries get 2 key splits: 511*8*2*130*4 = 4.25 MB > 4 MiB
+    assert 511 * 8 * 2 * 130 * 4 > sa.SA_DECODE_SCRATCH_BYTES
+    assert dec(Q, K, V, O, P, 511, 8, 1, 1, 4096, 128, w, None) == sa.SA_ERR_SCRATCH
     assert sa.strerror(sa.SA_ERR_SCRATCH) != "unknown status"
 
 

@@ -38,9 +38,10 @@ def decode_pair(gpu, spec, B, H, Hkv, n_new, C, d, seed):
 
 
 def test_noalloc_decode_matches_decode_on_two_calls(gpu):
-    # Call 1: the window-4096 serving shape (B=64, 32 query heads over 8 KV
-    # heads): 4 key splits, 4.3 MB of partials in the static scratch.
-    r1, n1 = decode_pair(gpu, "causal;window=4096", 64, 32, 8, 1, 4096, 128, seed=3)
+    # Call 1: the window-4096 serving shape with 16 sequences (32 query heads
+    # over 8 KV heads): 128 key groups get 4 key splits, 1.06 MB of partials
+    # in the static scratch.
+    r1, n1 = decode_pair(gpu, "causal;window=4096", 16, 32, 8, 1, 4096, 128, seed=3)
     # Call 2, smaller, right behind it on the same stream: 6 key splits over
     # a 1500-key window with 3 new tokens, d=64.
     r2, n2 = decode_pair(gpu, "causal;window=1500", 4, 8, 2, 3, 2000, 64, seed=4)
@@ -51,10 +52,10 @@ def test_noalloc_decode_matches_decode_on_two_calls(gpu):
 
 
 def test_noalloc_decode_refuses_past_the_scratch_limit(gpu):
-    """B=255, H=64, Hkv=8, d=128, window 4096: 2040 workgroups get 2 key
-    splits, 16.97 MB of partials, above the 16 MiB scratch: SA_ERR_SCRATCH,
-    with the output untouched."""
-    B, H, Hkv, C, d = 255, 64, 8, 4096, 128
+    """B=511, H=8, Hkv=1, d=128, window 4096: 511 key groups of 8 queries
+    get 2 key splits, 4.25 MB of partials, above the 4 MiB scratch:
+    SA_ERR_SCRATCH, with the output untouched."""
+    B, H, Hkv, C, d = 511, 8, 1, 4096, 128
     need = B * H * 1 * 2 * (d + 2) * 4
     assert need > gpu.SA_DECODE_SCRATCH_BYTES
     q = torch.zeros(B, H, 1, d, dtype=torch.bfloat16, device="cuda")
