@@ -364,17 +364,15 @@ __global__ __launch_bounds__(kThreads) void sa_bwd_dkv_kernel(BwdArgs b) {
 // ------------------------------------------- bf16: tiles by direct loads
 // For bf16 (d = 64, 128) the two kernels below (sa_bwd_dq_dma_kernel,
 // sa_bwd_dkv_dma_kernel) fill unpadded, XOR-swizzled row-major LDS tiles
-// with direct global->LDS loads (16 bytes per lane, 1 KiB per instruction),
+// with buffer loads straight into LDS (16 bytes per lane, 1 KiB per instruction),
 // double-buffered so that the next tile's loads run under the current
 // tile's MFMAs.  The transposed operands (K^T, Q^T, dO^T) are read from the
 // same row-major tiles with transposing LDS reads, so no transposed copy is
 // staged.  Each 64-row tile is processed as two 32-row halves.
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef const __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 typedef __attribute__((address_space(3))) s16x4* lptr_s16x4_t;
-__device__ __forceinline__ gptr_t as_global(const void* p) { return (gptr_t)p; }
 __device__ __forceinline__ lptr_t as_lds(void* p) { return (lptr_t)p; }
 __device__ __forceinline__ lptr_s16x4_t as_lds_s16x4(const void* p) { return (lptr_s16x4_t)(void*)p; }
 
@@ -402,38 +400,16 @@ __device__ __forceinline__ int swz(int r) {
         return ((r & 1) ? 2 : 0) ^ ((r & 2) ? 4 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 3 : 0);
 }
 
-// This wave's share of the direct loads of one 64-row tile of two [T][d]
-// tensors: LDS chunk position p of row r receives source chunk p ^ swz(r).
-// row_of(r) is the source row of tile row r (always a valid row).
-template <int D, int NW, typename RowOf>
-__device__ __forceinline__ void dma_rows2(__bf16* dst_a, __bf16* dst_b, const __bf16* src_a,
-                                          const __bf16* src_b, RowOf row_of, int wave, int lane) {
-    constexpr int CPR = D / 8;     // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;  // rows per instruction
-    constexpr int NJ = CPR / NW;   // instructions per wave (NW waves share the tile)
-    static_assert(CPR % NW == 0, "loads split evenly over the waves");
-    // Instruction j of this wave fills tile rows r0 + j * NW * RPI; the row's
-    // low four bits, hence its swizzle, do not depend on j.
-    const int r0 = wave * RPI + lane / CPR;
-    const int ch = (lane % CPR) ^ swz<D>(r0);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const size_t off = size_t(row_of(r0 + j * NW * RPI)) * D + ch * 8;
-        const int lds = (wave + j * NW) * 512;
-        __builtin_amdgcn_global_load_lds(as_global(src_a + off), as_lds(dst_a + lds), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(as_global(src_b + off), as_lds(dst_b + lds), 16, 0, 0);
-    }
-}
-
-// The same tile fill with buffer loads into LDS, for tiles of 64 keys.  The
-// rows of one wave's pieces are NW * RPI apart -- a multiple of 16, so every
-// piece of a lane has the same swizzled chunk -- and a piece's byte offset
-// from the tile's first row is the first piece's plus a scalar step.  Issuing
-// a tile of consecutive rows then takes a lane's first row r0 and that offset
-// (a few instructions from the lane id, recomputed at each issue so that
-// they hold no register across the loop), with the tile's first row and the
-// step as scalar offsets.  A tile past T clamps its rows to T - 1 per lane,
-// and a tile of listed rows takes per-lane offsets.
+// This wave's share of the loads of one 64-row tile of two [T][d] tensors,
+// by buffer loads into LDS: LDS chunk position p of row r receives source
+// chunk p ^ swz(r).  The rows of one wave's pieces are NW * RPI apart (a
+// multiple of 16, so every piece of a lane has the same swizzled chunk), and
+// a piece's byte offset from the tile's first row is the first piece's plus
+// a scalar step.  Issuing a tile of consecutive rows then takes a lane's
+// first row r0 and that offset (a few instructions from the lane id), with
+// the tile's first row and the step as scalar offsets.  A tile past T clamps
+// its rows to T - 1 per lane, and a tile of listed rows takes per-lane
+// offsets.
 template <int D, int NW>
 struct DmaTile {
     static constexpr int CPR = D / 8;     // 16-byte chunks per row
@@ -669,25 +645,41 @@ __global__ __launch_bounds__(NW * 64, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
         }
     };
     auto compute = [&](const BwdCursor& c, const E* kt, const E* vt) {
+        // The tile's allowed keys, and whether any is missing (wave-uniform:
+        // full tiles skip the per-score test).
         uint64_t aw = ~0ull;
+        bool msk;
         if (c.inplace()) {
             const int k0 = c.kb * kBK;
+            msk = c.masked;
             if (c.masked)
                 aw = allowed_word(a, qi, k0, rowg, ldc(a.colbits, k0 >> 6), qres,
                                   a.dil == 1 ? 0 : k0 % a.dil, qblk);
         } else {
+            msk = gtot - c.gi < kBK;
             aw = low_bits(gtot - c.gi);
         }
+        // Key reg_row(blk, r, h) of the tile is bit reg_row(blk, r, 0) of
+        // awh: one shift per tile, constant bit positions per score.
+        const uint64_t awh = aw >> (h * 8);
         // One 32-key half at a time: S^T, dP^T, dS^T, then dQ^T += K^T dS^T.
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             f32x16 sv = half_product<D>(kt, qf, blk, n, h);
             const f32x16 dp = half_product<D>(vt, gf, blk, n, h);
+            if (msk) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const bool ok = (aw >> reg_row(blk, r, h)) & 1;
-                const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sv[r], a.scale_log2, -lse2)) : 0.f;
-                sv[r] = p * (dp[r] - Dq);  // dS
+                for (int r = 0; r < 16; ++r) {
+                    const bool ok = (awh >> reg_row(blk, r, 0)) & 1;
+                    const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sv[r], a.scale_log2, -lse2)) : 0.f;
+                    sv[r] = p * (dp[r] - Dq);  // dS
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sv[r], a.scale_log2, -lse2));
+                    sv[r] = p * (dp[r] - Dq);  // dS
+                }
             }
             half_accumulate_tr<D>(acc, kt, sv, blk, lane);
         }
@@ -722,12 +714,10 @@ __global__ __launch_bounds__(NW * 64, 2) void sa_bwd_dq_dma_kernel(BwdArgs b) {
             cur = nxt;
         }
     } else {
-        // d = 128 at two waves per SIMD has no registers for a second copy
-        // of the loop body (it spills 224 bytes): the slot is chosen at run
-        // time, and a tile's reads of its slot then also wait for the loads
-        // into the other one, which the second wave of the SIMD covers.  (One
-        // wave per SIMD with two static slots fits in 296 registers but
-        // measured 11% slower on the 32K window layer.)
+        // d = 128: the slot is chosen at run time, so a tile's reads of its
+        // slot also wait for the loads into the other one, which the second
+        // wave of the SIMD covers.  Two static slots and an unrolled loop fit
+        // in 247 registers at two waves per SIMD but measured no faster.
         __shared__ __attribute__((aligned(1024))) E kbuf[2 * TILE];
         __shared__ __attribute__((aligned(1024))) E vbuf[2 * TILE];
         int slot = 0;
@@ -813,12 +803,18 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kerne
         }
     };
     enter();
+    // Query tiles and their LSE and D values by buffer loads.  (The
+    // flat-encoded global->LDS loads count against both wait counters, and
+    // the compiler turns every LDS wait behind one into a full drain.)
+    const DmaTile<D, NW> dt(wave, lane);
+    const __amdgpu_buffer_rsrc_t qrs = raw_rsrc(Qp, T * D * 2), grs = raw_rsrc(Gp, T * D * 2);
+    const __amdgpu_buffer_rsrc_t lrs = raw_rsrc(Lp, T * 4), drs = raw_rsrc(Dp, T * 4);
     auto issue = [&](int q0, E* qd, E* gd, float* lsd, float* dsd) {
-        dma_rows2<D, NW>(qd, gd, Qp, Gp, [&](int rr) { return min(q0 + rr, T - 1); }, wave, lane);
+        dt.rows_from(qrs, grs, qd, gd, q0, T);
         if (wave == 0) {
             const int i = min(q0 + lane, T - 1);
-            __builtin_amdgcn_global_load_lds(as_global(Lp + i), as_lds(lsd), 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(as_global(Dp + i), as_lds(dsd), 4, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, as_lds(lsd), 4, i * 4, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, as_lds(dsd), 4, i * 4, 0, 0, 0);
         }
     };
     auto compute = [&](int q0, bool msk, const E* qt_l, const E* gt_l, const float* ls, const float* dsv) {
@@ -838,22 +834,40 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 2 : 1) void sa_bwd_dkv_dma_kerne
             svs[blk] = half_product<D, D == 128>(qt_l, kf, blk, n, h);
             dps[blk] = half_product<D, D == 128>(gt_l, vf, blk, n, h);
         }
+        // Query reg_row(blk, r, h) of the tile is bit reg_row(blk, r, 0) of
+        // awh: one shift per tile, constant bit positions per score.
+        const uint64_t awh = aw >> (h * 8);
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             f32x16& sv = svs[blk];
             f32x16& dp = dps[blk];
+            if (msk) {
 #pragma unroll
-            for (int r4 = 0; r4 < 16; r4 += 4) {
-                const int x0 = reg_row(blk, r4, h);
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + x0);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsv + x0);
+                for (int r4 = 0; r4 < 16; r4 += 4) {
+                    const int x0 = reg_row(blk, r4, h);
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + x0);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsv + x0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool ok = (aw >> (x0 + e)) & 1;
-                    const float pv =
-                        ok ? __builtin_amdgcn_exp2f(fmaf(sv[r4 + e], a.scale_log2, -l4[e] * kLog2e)) : 0.f;
-                    sv[r4 + e] = pv;
-                    dp[r4 + e] = pv * (dp[r4 + e] - d4[e]);  // dS
+                    for (int e = 0; e < 4; ++e) {
+                        const bool ok = (awh >> (reg_row(blk, r4, 0) + e)) & 1;
+                        const float pv =
+                            ok ? __builtin_amdgcn_exp2f(fmaf(sv[r4 + e], a.scale_log2, -l4[e] * kLog2e)) : 0.f;
+                        sv[r4 + e] = pv;
+                        dp[r4 + e] = pv * (dp[r4 + e] - d4[e]);  // dS
+                    }
+                }
+            } else {  // wave-uniform: a full tile skips the per-score test
+#pragma unroll
+                for (int r4 = 0; r4 < 16; r4 += 4) {
+                    const int x0 = reg_row(blk, r4, h);
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + x0);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsv + x0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float pv = __builtin_amdgcn_exp2f(fmaf(sv[r4 + e], a.scale_log2, -l4[e] * kLog2e));
+                        sv[r4 + e] = pv;
+                        dp[r4 + e] = pv * (dp[r4 + e] - d4[e]);  // dS
+                    }
                 }
             }
             half_accumulate_tr<D, D == 128>(dv, gt_l, sv, blk, lane);
