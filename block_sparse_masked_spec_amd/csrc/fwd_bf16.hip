@@ -638,7 +638,11 @@ __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_
                rec[REC_FIRST_END] < 0, 0, gna + (rec[REC_GB1] - gb0)};
 
     auto run_tile = [&](const Cursor& c, const char* kt, const char* vt) {
-        const bool masked = !c.inplace() || c.masked;
+        // A full chunk of gathered keys needs no mask: only a chunk's unused
+        // slots are masked.  The 16x16x32 kernels mask every gathered tile
+        // all the same: skipping it there measured slower on layers without
+        // any gathered tile (the code moves).
+        const bool masked = c.inplace() ? c.masked : M16 || c.g_total - c.gi < kBK;
         uint64_t allowed[NQ];
         const int k0res = a.dil == 1 ? 0 : (c.kb * kBK) % a.dil;
 #pragma unroll
