@@ -228,3 +228,14 @@ def test_backward_bigbird_4k_full_size(gpu):
     spec = "blocks;block=64;radius=1;random=3;seed=0;global=0:128"
     heads_check(spec, *full_size(gpu, spec, 8, 12, 4096, 64, seed=1),
                 heads=[(0, 0), (3, 7), (7, 11)])
+
+
+def test_backward_longformer_16k_full_size(gpu):
+    """The Longformer 16K layer at full size (B=1, H=16, T=16384, d=64):
+    band, strided landmark keys and 128 global rows, whose plan splits the
+    global-row query block and runs the strided keys as gathered key blocks
+    in the dK/dV pass.  Three whole heads, the first and last included,
+    compared in full."""
+    spec = "bidir;radius=256;stride=16;phase=0;global=0:128"
+    heads_check(spec, *full_size(gpu, spec, 1, 16, 16384, 64, seed=2),
+                heads=[(0, 0), (0, 7), (0, 15)])

@@ -122,14 +122,15 @@ def test_key_splits_long_cache(gpu):
     run_decode(gpu, "causal;window=3000", 1, 8, 2, 2, 3001, 64, [3001], seed=8)
 
 
-def test_mistral_decode_batch_sampled(gpu):
-    """B=64, H=32, Hkv=8, d=128, window 4096, C=4096: the bench shape; six
-    sequences checked against the oracle."""
+def test_mistral_decode_batch_every_sequence(gpu):
+    """B=64, H=32, Hkv=8, d=128, window 4096, C=4096: the bench shape, in the
+    launch configuration the bench times; every sequence's 32 new rows
+    checked against the oracle."""
     rng = np.random.default_rng(0)
     pos = [int(x) for x in rng.integers(4096, 9000, size=64)]
     pos[0], pos[1] = 4095, 4096
-    run_decode(gpu, "causal;window=4096", 64, 32, 8, 1, 4096, 128, pos, seed=9,
-               check_rows=[0, 1, 2, 17, 40, 63])
+    worst = run_decode(gpu, "causal;window=4096", 64, 32, 8, 1, 4096, 128, pos, seed=9)
+    announce(f"decode bench shape, all 64 sequences: max abs err {worst:.3e}")
 
 
 @pytest.mark.parametrize("case", range(40))
