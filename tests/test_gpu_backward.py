@@ -239,3 +239,32 @@ def test_backward_longformer_16k_full_size(gpu):
     spec = "bidir;radius=256;stride=16;phase=0;global=0:128"
     heads_check(spec, *full_size(gpu, spec, 1, 16, 16384, 64, seed=2),
                 heads=[(0, 0), (0, 7), (0, 15)])
+
+
+def test_backward_at_max_length(gpu):
+    """T = SA_MAX_T = 2^22 (the longest sequence the library accepts), d = 128,
+    causal window of 256: Q, K, V, dO and each gradient of the sequence span
+    exactly 1 GiB.  The window rule depends on i - j only, so the oracle run
+    on a slice [a, b) of the sequence alone gives exact values for the rows
+    whose keys all lie in the slice (dQ and LSE of rows i >= a + 255, every
+    row when a = 0) and for the keys whose queries and those queries' keys
+    all lie in it (dK and dV of keys a + 255 <= j < b - 255, without the
+    first bound when a = 0 and without the second when b = T).  Slices at
+    the start, the middle and the end of the sequence are checked."""
+    T, d, W = 1 << 22, 128, 256
+    spec = f"causal;window={W}"
+    q, k, v = inputs.qkv(1, 1, T, d, "bf16", 13)
+    g = inputs.qkv(1, 1, T, d, "bf16", 513)[0]
+    _, lse, dq, dk, dv = run(gpu, spec, q, k, v, g)
+    for a, b in ((0, 4096), (T // 2 - 2048, T // 2 + 2048), (T - 4096, T)):
+        announce(f"oracle bwd {spec} T={T} slice {a}..{b}")
+        sl = (slice(None), slice(None), slice(a, b))
+        qs, ks, vs, gs = (x[sl].contiguous() for x in (q, k, v, g))
+        _, lse_ref, _ = oracle.forward_rows(spec, qs, ks, vs)
+        rq, rk, rv = oracle.backward(spec, qs, ks, vs, gs)
+        r0 = 0 if a == 0 else W - 1            # first exact row (slice index)
+        k1 = (b - a) if b == T else (b - a) - (W - 1)  # one past the last exact key
+        assert np.abs(lse[0, 0, a + r0:b].double().numpy() - lse_ref[0, 0, r0:]).max() <= 2.0 ** -8
+        check_grad(dq[:, :, a + r0:b], rq[:, :, r0:], "bf16", f"dQ max length rows {a + r0}..{b - 1}")
+        check_grad(dk[:, :, a + r0:a + k1], rk[:, :, r0:k1], "bf16", f"dK max length keys {a + r0}..{a + k1 - 1}")
+        check_grad(dv[:, :, a + r0:a + k1], rv[:, :, r0:k1], "bf16", f"dV max length keys {a + r0}..{a + k1 - 1}")
