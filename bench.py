@@ -560,7 +560,7 @@ def main():
     E_total = sum(allowed) * B * H  # allowed (b,h,i,j) pairs per step
     flops = 4.0 * d * E_total
     alg_bytes = 4.0 * B * H * T * d * (2 if dtype == "bf16" else 4) * len(specs)
-    info = [sa.sparse_attn_plan_info(s, T, d, sa.SA_DTYPE_BF16 if dtype == "bf16" else sa.SA_DTYPE_F32)
+    info = [sa.sparse_attn_plan_info_bh(s, B, H, T, d, sa.SA_DTYPE_BF16 if dtype == "bf16" else sa.SA_DTYPE_F32)
             for s in specs]
     executed = sum(i["executed_cells"] for i in info) * B * H
     # Plans that split heavy query blocks add a merge kernel to each call.

@@ -39,7 +39,7 @@ SA_MAX_GLOBAL_RANGES = 64
 
 EXPORTED = [
     "sparse_attn_fwd", "sparse_attn_fwd_f32", "sparse_attn_parse", "sparse_attn_count",
-    "sparse_attn_tile_map", "sparse_attn_tile_shape", "sparse_attn_plan_info",
+    "sparse_attn_tile_map", "sparse_attn_tile_shape", "sparse_attn_plan_info", "sparse_attn_plan_info_bh",
     "sparse_attn_strerror", "sparse_attn_release_cache", "sparse_attn_decode",
     "sparse_attn_decode_cache_rows", "sparse_attn_fwd_lse", "sparse_attn_fwd_lse_f32",
     "sparse_attn_bwd", "sparse_attn_bwd_f32", "sparse_attn_decode_noalloc",
@@ -103,6 +103,8 @@ def load():
     lib.sparse_attn_tile_shape.restype = i32
     lib.sparse_attn_plan_info.argtypes = [cs, i32, i32, i32, ctypes.POINTER(sa_plan_info)]
     lib.sparse_attn_plan_info.restype = i32
+    lib.sparse_attn_plan_info_bh.argtypes = [cs, i32, i32, i32, i32, i32, ctypes.POINTER(sa_plan_info)]
+    lib.sparse_attn_plan_info_bh.restype = i32
     lib.sparse_attn_strerror.argtypes = [i32]
     lib.sparse_attn_strerror.restype = cs
     lse_args = [vp, vp, vp, vp, vp, i32, i32, i32, i32, cs, vp]
@@ -211,6 +213,13 @@ def sparse_attn_plan_info(mask_spec, T, d, dtype=SA_DTYPE_BF16) -> dict:
     info = sa_plan_info()
     _check(load().sparse_attn_plan_info(_spec(mask_spec), T, d, dtype, ctypes.byref(info)),
            "sparse_attn_plan_info")
+    return {name: getattr(info, name) for name, _ in sa_plan_info._fields_}
+
+
+def sparse_attn_plan_info_bh(mask_spec, B, H, T, d, dtype=SA_DTYPE_BF16) -> dict:
+    info = sa_plan_info()
+    _check(load().sparse_attn_plan_info_bh(_spec(mask_spec), B, H, T, d, dtype, ctypes.byref(info)),
+           "sparse_attn_plan_info_bh")
     return {name: getattr(info, name) for name, _ in sa_plan_info._fields_}
 
 

@@ -387,7 +387,7 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     const int sub = sa::residue_split(m, T, d, dtype) ? m.dilation : 1;
     if (sub > 1) m.dilation = 1;
     const int Ts = T / sub;
-    const int bq = sa::fwd_query_block(m, d, dtype);
+    const int bq = sa::fwd_query_block_bh(m, d, dtype, BH, Ts, sub);
     // Only the bf16 fast path runs split plans (and leaves them for the
     // merge kernel).
     const bool fast = sa::fwd_fast_path(dtype, d, bq, sub);
@@ -800,40 +800,57 @@ SA_EXPORT int sparse_attn_tile_shape(const char* mask_spec, int d, int dtype, in
     });
 }
 
+namespace {
+
+// The plan of a forward call of BH sequences (BH < 0: a call whose grid
+// fills the chip, the plan sparse_attn_plan_info describes).
+int plan_info_for(const char* mask_spec, int64_t BH, int T, int d, int dtype, sa_plan_info* info) {
+    if (!info) return SA_ERR_NULL;
+    int bq = 0, bk = 0;
+    int rc = sparse_attn_tile_shape(mask_spec, d, dtype, &bq, &bk);
+    if (rc != SA_OK) return rc;
+    sa_mask m;
+    rc = parse_for(mask_spec, T, &m);
+    if (rc != SA_OK) return rc;
+    MaskRule rule(m, T);
+    // The plan the forward runs: for a residue split, one subsequence's.
+    const int sub = sa::residue_split(m, T, d, dtype) ? m.dilation : 1;
+    sa_mask mp = m;
+    if (sub > 1) mp.dilation = 1;
+    if (BH >= 0) bq = sa::fwd_query_block_bh(mp, d, dtype, BH, T / sub, sub);
+    MaskRule prule(mp, T / sub);
+    HostPlan hp = sa::build_plan(prule, bq, bk,
+                                 sub == 1 && sa::fwd_fast_path(dtype, d, bq, sub) ? split_cap() : 0);
+    std::memset(info, 0, sizeof(*info));
+    info->bq = bq;
+    info->bk = bk;
+    info->n_qb = hp.n_qb;
+    info->n_kb = hp.n_kb;
+    info->subsequences = sub;
+    info->split_parts = hp.n_parts;
+    info->inplace_tiles = hp.inplace_tiles * sub;
+    info->masked_tiles = hp.masked_tiles * sub;
+    info->gathered_tiles = hp.gathered_tiles * sub;
+    info->gathered_keys = hp.gathered_keys * sub;
+    info->executed_cells = int64_t(bq) * bk * (hp.inplace_tiles + hp.gathered_tiles) * sub;
+    int64_t total = 0;
+    for (int64_t i = 0; i < T; ++i) total += rule.allowed_in(i, 0, T);
+    info->allowed_cells = total;
+    return SA_OK;
+}
+
+}  // namespace
+
 SA_EXPORT int sparse_attn_plan_info(const char* mask_spec, int T, int d, int dtype,
                                     sa_plan_info* info) {
+    return guarded([&] { return plan_info_for(mask_spec, -1, T, d, dtype, info); });
+}
+
+SA_EXPORT int sparse_attn_plan_info_bh(const char* mask_spec, int B, int H, int T, int d, int dtype,
+                                       sa_plan_info* info) {
     return guarded([&] {
-        if (!info) return SA_ERR_NULL;
-        int bq = 0, bk = 0;
-        int rc = sparse_attn_tile_shape(mask_spec, d, dtype, &bq, &bk);
-        if (rc != SA_OK) return rc;
-        sa_mask m;
-        rc = parse_for(mask_spec, T, &m);
-        if (rc != SA_OK) return rc;
-        MaskRule rule(m, T);
-        // The plan the forward runs: for a residue split, one subsequence's.
-        const int sub = sa::residue_split(m, T, d, dtype) ? m.dilation : 1;
-        sa_mask mp = m;
-        if (sub > 1) mp.dilation = 1;
-        MaskRule prule(mp, T / sub);
-        HostPlan hp = sa::build_plan(prule, bq, bk,
-                                     sub == 1 && sa::fwd_fast_path(dtype, d, bq, sub) ? split_cap() : 0);
-        std::memset(info, 0, sizeof(*info));
-        info->bq = bq;
-        info->bk = bk;
-        info->n_qb = hp.n_qb;
-        info->n_kb = hp.n_kb;
-        info->subsequences = sub;
-        info->split_parts = hp.n_parts;
-        info->inplace_tiles = hp.inplace_tiles * sub;
-        info->masked_tiles = hp.masked_tiles * sub;
-        info->gathered_tiles = hp.gathered_tiles * sub;
-        info->gathered_keys = hp.gathered_keys * sub;
-        info->executed_cells = int64_t(bq) * bk * (hp.inplace_tiles + hp.gathered_tiles) * sub;
-        int64_t total = 0;
-        for (int64_t i = 0; i < T; ++i) total += rule.allowed_in(i, 0, T);
-        info->allowed_cells = total;
-        return SA_OK;
+        if (B < 1 || H < 1) return SA_ERR_SHAPE;
+        return plan_info_for(mask_spec, int64_t(B) * H, T, d, dtype, info);
     });
 }
 

@@ -815,7 +815,13 @@ int launch_fwd_fast(int dtype, int d, const FwdArgs& a, int64_t grid, void* stre
         if (d == 64) return launch_t<64, 1, 4, true>(a, grid, stream);
         return SA_ERR_UNSUPPORTED;
     }
-    if (a.bq == 64) return d == 64 ? launch_t<64, 1, 2>(a, grid, stream) : SA_ERR_UNSUPPORTED;
+    if (a.bq == 64) {
+        if (d != 64) return SA_ERR_UNSUPPORTED;
+        // token level: the small grids that the 64-row plans are chosen for
+        // (four 16-query waves); block mode: two 32-query waves
+        if (a.blk == 0) return launch_t<64, 1, 4, false, 16>(a, grid, stream);
+        return launch_t<64, 1, 2>(a, grid, stream);
+    }
     if (d == 128) return launch_t<128, 1, 4>(a, grid, stream);
     if (d == 64 && grid <= SA_FWD_SMALL_GRID) return launch_t<64, 1, 8, false, 16>(a, grid, stream);
     if (d == 64) return launch_t<64, 1, 4>(a, grid, stream);

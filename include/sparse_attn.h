@@ -245,18 +245,32 @@ int sparse_attn_tile_map(const char* mask_spec, int T, int bq, int bk,
                          uint8_t* map);
 
 /* The tile shape (query rows bq x keys bk) the forward kernel uses for
- * mask_spec, head dim d and dtype (SA_DTYPE_*); the same shape that
- * sparse_attn_plan_info reports.  mask_spec may be NULL: the shape of the
- * token-level specs (causal / bidir), 128 x 64.  Block mode with a block
- * size that is a multiple of 64 but not of 128 runs 64 x 64 tiles at bf16,
- * d = 64 (every tile then lies in one query block).  Host only.  Returns
- * SA_OK or SA_ERR_{NULL, UNSUPPORTED, SPEC, RANGE}. */
+ * mask_spec, head dim d and dtype (SA_DTYPE_*) in a call large enough to
+ * fill the GPU; the same shape that sparse_attn_plan_info reports.
+ * mask_spec may be NULL: the shape of the token-level specs (causal /
+ * bidir), 128 x 64.  Block mode with a block size that is a multiple of 64
+ * but not of 128 runs 64 x 64 tiles at bf16, d = 64 (every tile then lies in
+ * one query block).  A smaller call can run other tiles: the shape of a
+ * given call is the bq, bk that sparse_attn_plan_info_bh reports for its B,
+ * H and T.  Host only.  Returns SA_OK or SA_ERR_{NULL, UNSUPPORTED, SPEC,
+ * RANGE}. */
 int sparse_attn_tile_shape(const char* mask_spec, int d, int dtype, int* bq, int* bk);
 
-/* Describe the plan the kernel would run (host only; builds no device
- * state). */
+/* Describe the plan the kernel would run for (mask_spec, T, d, dtype) in a
+ * call large enough to fill the GPU (host only; builds no device state).
+ * Returns SA_OK or SA_ERR_{NULL, SHAPE, UNSUPPORTED, SPEC, RANGE}. */
 int sparse_attn_plan_info(const char* mask_spec, int T, int d, int dtype,
                           sa_plan_info* info);
+
+/* Describe the plan a forward call with these B, H, T, d, dtype runs (host
+ * only; builds no device state).  It differs from sparse_attn_plan_info in
+ * one case: a token-level (causal / bidir) bf16 call with d = 64, no residue
+ * split and B * H * ceil(T / 128) <= 256 (the MI355X's compute units) runs
+ * 64 x 64 tiles, so that every compute unit holds two independent
+ * workgroups.  Returns SA_OK or SA_ERR_{NULL, SHAPE (B or H < 1, bad T),
+ * UNSUPPORTED, SPEC, RANGE}. */
+int sparse_attn_plan_info_bh(const char* mask_spec, int B, int H, int T, int d, int dtype,
+                             sa_plan_info* info);
 
 /*
  * Windowed decode, bf16: n_new new query tokens per sequence against a

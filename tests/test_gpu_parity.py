@@ -187,6 +187,16 @@ def test_cfg_code_model_layer(gpu, spec, seed):
     full_check(gpu, spec, 8, 8, 512, 64, "bf16", seed)
 
 
+@pytest.mark.parametrize("T,bq", [(4096, 64), (4097, 128)])
+def test_small_grid_64_row_tiles_and_the_limit(gpu, T, bq):
+    """Token-level bf16 d = 64 calls: at B*H*ceil(T/128) = 256 the call runs
+    64 x 64 tiles (four 16-query waves per workgroup); one 128-row block more
+    and it runs 128-row blocks again.  Every output compared."""
+    spec = "causal;window=256;stride=64;phase=0;global=7"
+    assert gpu.sparse_attn_plan_info_bh(spec, 2, 4, T, 64)["bq"] == bq
+    full_check(gpu, spec, 2, 4, T, 64, "bf16", seed=T)
+
+
 # ------------------------------------------------ large configs, sampled rows
 def sampled_rows(B, H, T, rng, extra=()):
     rows = set()
@@ -284,7 +294,7 @@ def test_split_blocks_forced(gpu, monkeypatch, spec, T, d, cap):
     merged: in-place runs cut mid-run and gathered key lists cut at any
     tile, against the oracle (O and LSE)."""
     monkeypatch.setenv("SA_FWD_SPLIT_TILES", str(cap))
-    info = gpu.sparse_attn_plan_info(spec, T, d)
+    info = gpu.sparse_attn_plan_info_bh(spec, 2, 3, T, d)  # the plan this call runs
     assert info["split_parts"] > 0
     lse_check(gpu, spec, 2, 3, T, d, seed=cap)
 

@@ -182,6 +182,39 @@ def test_tile_shape_agrees_with_plan_info():
     assert e.value.status == sa.SA_ERR_SPEC
 
 
+def test_plan_info_bh_small_token_level_d64_calls_run_64_row_tiles():
+    """A call's own plan: token-level bf16 d = 64 calls whose 128-row blocks
+    number at most 256 over all (b, h) (the MI355X's compute units) run 64 x
+    64 tiles; every other call runs the plan sparse_attn_plan_info reports
+    (which describes calls large enough to fill the GPU)."""
+    small = [
+        ("causal;window=128;stride=64;phase=0", 8, 8, 512),   # the 512-token code layer
+        ("causal", 8, 8, 512),
+        ("bidir;radius=40;stride=16;global=0:128", 1, 2, 16384),  # 2 x 128 blocks: at the limit
+    ]
+    for spec, B, H, T in small:
+        got = sa.sparse_attn_plan_info_bh(spec, B, H, T, 64)
+        assert (got["bq"], got["bk"]) == (64, 64), spec
+        assert got["n_qb"] == -(-T // 64)
+        assert got["allowed_cells"] == sa.sparse_attn_plan_info(spec, T, 64)["allowed_cells"]
+    large = [
+        ("bidir;radius=40;stride=16;global=0:128", 1, 2, 16385, 64, sa.SA_DTYPE_BF16),  # 2 x 129 blocks
+        ("causal;window=128", 8, 8, 4096, 64, sa.SA_DTYPE_BF16),
+        ("causal;window=128", 8, 8, 512, 128, sa.SA_DTYPE_BF16),     # d = 128
+        ("causal;window=128", 8, 8, 512, 64, sa.SA_DTYPE_F32),       # fp32
+        ("causal;window=128;dilation=2", 1, 2, 512, 64, sa.SA_DTYPE_BF16),  # residue split
+        ("blocks;block=64;radius=1;random=3;seed=0;global=0:128", 8, 12, 4096, 64, sa.SA_DTYPE_BF16),
+        ("causal;window=4096", 1, 32, 32768, 128, sa.SA_DTYPE_BF16),
+    ]
+    for spec, B, H, T, d, dt in large:
+        assert sa.sparse_attn_plan_info_bh(spec, B, H, T, d, dt) == sa.sparse_attn_plan_info(spec, T, d, dt), spec
+    lib = sa.load()
+    info = sa.sa_plan_info()
+    assert lib.sparse_attn_plan_info_bh(b"causal", 0, 1, 16, 64, 0, ctypes.byref(info)) == sa.SA_ERR_SHAPE
+    assert lib.sparse_attn_plan_info_bh(b"causal", 1, 0, 16, 64, 0, ctypes.byref(info)) == sa.SA_ERR_SHAPE
+    assert lib.sparse_attn_plan_info_bh(b"causal", 1, 1, 16, 64, 0, None) == sa.SA_ERR_NULL
+
+
 def test_parser_fields_and_normalisation():
     m = sa.sparse_attn_parse(" bidir ; radius = 2 ; stride=16;global = 7:9 , 0 , 8:12 ,3")
     assert (m.causal, m.has_radius, m.radius, m.stride, m.phase) == (0, 1, 2, 16, 0)
