@@ -360,6 +360,24 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
+// Compute units of one MI355X.
+constexpr int64_t kCUs = 256;
+
+// Query rows per tile of the forward for a call of BH sequences of T rows
+// (T of one subsequence when a residue split runs `sub` of them).  A
+// token-level bf16 d = 64 call whose 128-row blocks would not give every CU
+// a workgroup runs 64-row blocks instead, four 16-query waves each: twice
+// the workgroups, so that each CU holds two whose barriers are independent
+// and one's waits are filled by the other's work (with one eight-wave
+// workgroup per CU, both waves of a SIMD wait at the same barrier).
+int fwd_query_block_bh(const sa_mask& m, int d, int dtype, int64_t BH, int64_t T, int sub) {
+    const int bq = sa::fwd_query_block(m, d, dtype);
+    if (bq == sa::kBQ && m.block == 0 && dtype == SA_DTYPE_BF16 && d == 64 && sub == 1 && BH >= 1 &&
+        BH <= kCUs && BH * ((T + sa::kBQ - 1) / sa::kBQ) <= kCUs)
+        return 64;
+    return bq;
+}
+
 int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int B, int H, int T,
             int d, const char* spec, void* stream, float* lse = nullptr) {
     if (!Q || !K || !V || !O || !spec) return SA_ERR_NULL;
@@ -387,7 +405,7 @@ int forward(int dtype, const void* Q, const void* K, const void* V, void* O, int
     const int sub = sa::residue_split(m, T, d, dtype) ? m.dilation : 1;
     if (sub > 1) m.dilation = 1;
     const int Ts = T / sub;
-    const int bq = sa::fwd_query_block_bh(m, d, dtype, BH, Ts, sub);
+    const int bq = fwd_query_block_bh(m, d, dtype, BH, Ts, sub);
     // Only the bf16 fast path runs split plans (and leaves them for the
     // merge kernel).
     const bool fast = sa::fwd_fast_path(dtype, d, bq, sub);
@@ -817,7 +835,7 @@ int plan_info_for(const char* mask_spec, int64_t BH, int T, int d, int dtype, sa
     const int sub = sa::residue_split(m, T, d, dtype) ? m.dilation : 1;
     sa_mask mp = m;
     if (sub > 1) mp.dilation = 1;
-    if (BH >= 0) bq = sa::fwd_query_block_bh(mp, d, dtype, BH, T / sub, sub);
+    if (BH >= 0) bq = fwd_query_block_bh(mp, d, dtype, BH, T / sub, sub);
     MaskRule prule(mp, T / sub);
     HostPlan hp = sa::build_plan(prule, bq, bk,
                                  sub == 1 && sa::fwd_fast_path(dtype, d, bq, sub) ? split_cap() : 0);

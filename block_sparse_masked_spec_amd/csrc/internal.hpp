@@ -329,24 +329,6 @@ inline int fwd_query_block(const sa_mask& m, int d, int dtype) {
                : kBQ;
 }
 
-// Compute units of one MI355X.
-constexpr int64_t kCUs = 256;
-
-// Query rows per tile of the forward for a call of BH sequences of T rows
-// (T of one subsequence when a residue split runs `sub` of them).  A
-// token-level bf16 d = 64 call whose 128-row blocks would not give every CU
-// a workgroup runs 64-row blocks instead, four 16-query waves each: twice
-// the workgroups, so that each CU holds two whose barriers are independent
-// and one's waits are filled by the other's work (with one eight-wave
-// workgroup per CU, both waves of a SIMD wait at the same barrier).
-inline int fwd_query_block_bh(const sa_mask& m, int d, int dtype, int64_t BH, int64_t T, int sub) {
-    const int bq = fwd_query_block(m, d, dtype);
-    if (bq == kBQ && m.block == 0 && dtype == SA_DTYPE_BF16 && d == 64 && sub == 1 && BH >= 1 &&
-        BH <= kCUs && BH * ((T + kBQ - 1) / kBQ) <= kCUs)
-        return 64;
-    return bq;
-}
-
 // Whether the bf16 fast path runs (dtype, d) with bq-row tiles and `sub`
 // interleaved subsequences; only its plans are split.
 inline bool fwd_fast_path(int dtype, int d, int bq, int sub) {
