@@ -6,8 +6,9 @@
 // sliding-window attention", getnybble.com, "Implementation").  What differs
 // is how a tile is fed to the matrix cores:
 //
-//   * a workgroup of NW wavefronts covers the query block (128 rows, or 64
-//     with two waves); each wave owns 32 queries.  At d = 64 they are one
+//   * a workgroup of NW wavefronts covers the query block of 128 rows; each
+//     wave owns 32 queries (16 on the 64-row plans and on small grids, see
+//     below).  At d = 64 they are one
 //     32-wide MFMA column block (v_mfma_f32_32x32x16_bf16, NG groups of 32;
 //     the launches use NG = 1).  At d = 128 they are two 16-query blocks of
 //     v_mfma_f32_16x16x32_bf16: the same work in twice as many MFMAs of half
@@ -577,8 +578,11 @@ struct Occupancy {
 };
 
 // QW: queries per wave.  32: NG groups of 32 (d = 64) or two 16-query
-// blocks (d = 128); 16: one 16-query block per wave, for grids too small to
-// give each SIMD two waves otherwise (eight waves cover a 128-query block).
+// blocks (d = 128); 16: one 16-query block per wave, at d = 64 on the 64-row
+// plans (four waves: block mode with 64-key blocks, and token-level calls
+// whose 128-row blocks would not give every CU a workgroup) and on grids of
+// up to 512 128-row blocks (eight waves), where 32-query waves would leave
+// SIMDs with one wave.
 template <int D, int NG, int NW, bool SUB, int QW>
 __global__ __launch_bounds__(NW * 64, Occupancy<NG>::kWavesPerSimd) void sa_fwd_bf16_kernel(FwdArgs a) {
     constexpr int BQ = NW * NG * QW;  // waves x queries per wave = one query block
@@ -815,13 +819,9 @@ int launch_fwd_fast(int dtype, int d, const FwdArgs& a, int64_t grid, void* stre
         if (d == 64) return launch_t<64, 1, 4, true>(a, grid, stream);
         return SA_ERR_UNSUPPORTED;
     }
-    if (a.bq == 64) {
-        if (d != 64) return SA_ERR_UNSUPPORTED;
-        // token level: the small grids that the 64-row plans are chosen for
-        // (four 16-query waves); block mode: two 32-query waves
-        if (a.blk == 0) return launch_t<64, 1, 4, false, 16>(a, grid, stream);
-        return launch_t<64, 1, 2>(a, grid, stream);
-    }
+    // 64-row plans (block mode with 64-key blocks, and token-level calls
+    // too small to fill the GPU): four 16-query waves per block.
+    if (a.bq == 64) return d == 64 ? launch_t<64, 1, 4, false, 16>(a, grid, stream) : SA_ERR_UNSUPPORTED;
     if (d == 128) return launch_t<128, 1, 4>(a, grid, stream);
     if (d == 64 && grid <= SA_FWD_SMALL_GRID) return launch_t<64, 1, 8, false, 16>(a, grid, stream);
     if (d == 64) return launch_t<64, 1, 4>(a, grid, stream);
