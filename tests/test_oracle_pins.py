@@ -421,8 +421,9 @@ def test_dilated_bidir_rows_have_2r_plus_1_keys():
 
 # ------------------------------------------------------- block mode (BigBird)
 # "Sparse and sliding-window attention", section "Block-sparse attention:
-# BigBird": a local window of 3 blocks (W = 192 at block size 64), R = 3
-# random blocks and G = 2 global blocks; cost per token W + R + G.
+# BigBird": each query block reads a window of 3 blocks (W = 192 keys at
+# block size 64), three blocks drawn at random (R) and the two global ones
+# (G), so a token costs W + R + G reads.
 BIGBIRD = "blocks;block=64;radius=1;random=3;seed=0;global=0:128"
 SPLITMIX = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "splitmix64.json")))
 
